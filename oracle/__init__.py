@@ -1,0 +1,35 @@
+"""CPU oracle for packed variable-length attention (test infrastructure only).
+
+This package is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it.  The library under
+``variable_length_packed_pack_amd/`` never imports it, and the oracle shares no
+code with that library: no kernels, no helpers, no constants.
+
+Every function here is a plain, slow, obviously correct restatement of a
+definition from the pages:
+
+* ``pack_sequences``      -- "gigl.nn.packed_attention", "Data flow of a packed
+                             forward" and "Example".
+* ``grid_capacity``       -- "So you wanna CUDA Graph", "Scheduling without
+                             max_seqlen" (the launch-capacity bound G_cap).
+* ``build_ragged_grid``   -- "PyCoRa", section "CoRa Metadata"; "So you wanna
+                             CUDA Graph", "Scheduling without max_seqlen"
+                             (chunk_offsets prefix sum and its decode).
+* ``decode_tile``         -- the same section's flat-chunk decode.
+* ``varlen_attention``    -- "PyCoRa", "Ragged Flash Attention" (exact attention
+                             per sequence); "gigl.nn.packed_attention" (each
+                             sequence attends only to itself; first-token
+                             queries).
+
+All pins are in ``tests/test_oracle.py``; no oracle function is "parity unpinned".
+"""
+
+from .varlen_oracle import (  # noqa: F401
+    INT32_MAX,
+    build_ragged_grid,
+    decode_tile,
+    grid_capacity,
+    pack_sequences,
+    varlen_attention,
+    varlen_attention_rows,
+)

@@ -1,0 +1,278 @@
+"""Plain fp64 / integer oracle for packed variable-length attention.
+
+Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the library.
+
+The oracle takes arrays in and gives arrays out; it draws no random numbers and
+reads no files.  Integer metadata is built with pure-Python loops; attention is
+numpy float64, one (sequence, head) at a time, with a two-pass softmax (first
+the row maximum, then the exponentials), not the online softmax the GPU uses.
+
+Readings taken where the pages leave a point open (each also listed in the
+design notes of the repository):
+
+* flat_index is int64 and indexes the row-major padded grid
+  ``[num_seqs, max_seq_len]``: token j of sequence i is ``i*max_seq_len + j``.
+* block_offsets has ``num_seqs + 1`` entries with a leading 0, the last one
+  being the number of active tiles.
+* A tile belongs to the unique sequence i with
+  ``block_offsets[i] <= f < block_offsets[i+1]``; zero-length sequences own no
+  tile.
+* tile_order (longest sequence first): sequences sorted by length, longest
+  first, ties to the lower index; each contributes its tiles from the last
+  local tile down to local tile 0.
+* causal masking is in local positions, aligned bottom-right when the query
+  and key lengths differ: key j is visible to query p iff
+  ``j <= p + (Lk - Lq)``.  A first-token query sits at position 0.
+* lse is the natural log of the softmax denominator, ``[H, rows_q]``, and is
+  -inf (with a zero output row) when a query sees no key.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+INT32_MAX = 2**31 - 1
+
+
+# ---------------------------------------------------------------------------
+# Packing ("gigl.nn.packed_attention": "Data flow of a packed forward",
+# "Example", "Constraints")
+# ---------------------------------------------------------------------------
+
+def pack_sequences(lengths, max_seq_len: int):
+    """lengths -> (flat_index int64 [T], cu_seqlens int32 [B+1]).
+
+    cu_seqlens[0] = 0 and cu_seqlens[i+1] = cu_seqlens[i] + lengths[i]; the
+    packed buffer is ``padded_grid.flatten()[flat_index]``, so flat_index lists,
+    sequence after sequence, the row-major positions of the real tokens in the
+    padded ``[B, max_seq_len]`` grid.  Every length must be >= 1 (empty
+    sequences are unsupported on that page) and <= max_seq_len, and the token
+    count must fit in int32 because cu_seqlens is int32.
+    """
+    lengths = [int(x) for x in np.asarray(lengths).reshape(-1).tolist()]
+    if len(lengths) < 1:
+        raise ValueError("need at least one sequence")
+    if max_seq_len < 1:
+        raise ValueError("max_seq_len must be >= 1")
+    cu = [0]
+    for i, n in enumerate(lengths):
+        if n < 1:
+            raise ValueError(f"sequence {i} has length {n} < 1")
+        if n > max_seq_len:
+            raise ValueError(f"sequence {i} has length {n} > max_seq_len {max_seq_len}")
+        cu.append(cu[-1] + n)
+        if cu[-1] > INT32_MAX:
+            raise OverflowError("token count does not fit in int32")
+    flat = []
+    for i, n in enumerate(lengths):
+        for j in range(n):
+            flat.append(i * max_seq_len + j)
+    return np.asarray(flat, dtype=np.int64), np.asarray(cu, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Ragged grid ("PyCoRa": "CoRa Metadata"; "So you wanna CUDA Graph":
+# "Scheduling without max_seqlen")
+# ---------------------------------------------------------------------------
+
+def grid_capacity(total_tokens: int, num_seqs: int, block_m: int) -> int:
+    """G_cap(T, N, C) = M_max + floor((T - M_max) / C) with M_max = min(T, N).
+
+    The page proves this bounds the number of active tiles for any split of at
+    most T tokens over at most N sequences.
+    """
+    m_max = min(total_tokens, num_seqs)
+    return m_max + (total_tokens - m_max) // block_m
+
+
+def _tiles_of(length: int, block_m: int) -> int:
+    """ceil(length / block_m), applied per sequence (chunking restarts at
+    every sequence boundary), with integer arithmetic only."""
+    tiles = 0
+    covered = 0
+    while covered < length:
+        tiles += 1
+        covered += block_m
+    return tiles
+
+
+def build_ragged_grid(cu_seqlens, block_m: int):
+    """cu_seqlens -> (block_offsets [B+1], grid_mapping [G], tile_order [G]), int32.
+
+    block_offsets[0] = 0, block_offsets[i+1] = block_offsets[i] + ceil(len_i/C)
+    (the page's chunk_offsets); grid_mapping[f] is the sequence owning flat
+    tile f; tile_order lists flat tiles longest sequence first (see module
+    docstring).
+    """
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1).tolist()]
+    if len(cu) < 2 or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0 and have at least 2 entries")
+    if block_m < 1:
+        raise ValueError("block_m must be >= 1")
+    num_seqs = len(cu) - 1
+    lengths = []
+    for i in range(num_seqs):
+        n = cu[i + 1] - cu[i]
+        if n < 0:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        lengths.append(n)
+
+    block_offsets = [0]
+    for n in lengths:
+        block_offsets.append(block_offsets[-1] + _tiles_of(n, block_m))
+
+    grid_mapping = []
+    for i in range(num_seqs):
+        for _ in range(block_offsets[i], block_offsets[i + 1]):
+            grid_mapping.append(i)
+
+    seq_order = sorted(range(num_seqs), key=lambda i: (-lengths[i], i))
+    tile_order = []
+    for i in seq_order:
+        for t in reversed(range(block_offsets[i + 1] - block_offsets[i])):
+            tile_order.append(block_offsets[i] + t)
+
+    return (np.asarray(block_offsets, dtype=np.int32),
+            np.asarray(grid_mapping, dtype=np.int32),
+            np.asarray(tile_order, dtype=np.int32))
+
+
+def decode_tile(block_offsets, cu_seqlens, flat_tile: int, block_m: int):
+    """Flat tile -> (sequence, local tile, first packed token).
+
+    sequence = (first index whose block_offsets entry exceeds flat_tile) - 1,
+    local = flat_tile - block_offsets[sequence],
+    token_start = cu_seqlens[sequence] + local * C.
+    """
+    bo = [int(x) for x in np.asarray(block_offsets).tolist()]
+    first_greater = None
+    for idx, val in enumerate(bo):
+        if val > flat_tile:
+            first_greater = idx
+            break
+    if first_greater is None:
+        raise IndexError("flat tile beyond the active tiles")
+    seq = first_greater - 1
+    local = flat_tile - bo[seq]
+    start = int(np.asarray(cu_seqlens)[seq]) + local * block_m
+    return seq, local, start
+
+
+# ---------------------------------------------------------------------------
+# Attention ("PyCoRa": "Ragged Flash Attention"; "gigl.nn.packed_attention":
+# "packed_attention" and "Example")
+# ---------------------------------------------------------------------------
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor: widen exactly through float32
+        x = x.detach().float().cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _visibility(positions, lq: int, lk: int, causal: bool) -> np.ndarray:
+    """[Rq, Lk] boolean: key j visible to the query at local position p.
+
+    Non-causal: every key of the sequence.  Causal: j <= p + (Lk - Lq).
+    """
+    p = np.asarray(positions, dtype=np.int64)[:, None]
+    j = np.arange(lk, dtype=np.int64)[None, :]
+    if not causal:
+        return np.ones((p.shape[0], lk), dtype=bool)
+    return j <= p + (lk - lq)
+
+
+def _attend_one(qi, ki, vi, scale: float, causal: bool, positions, lq: int):
+    """Exact softmax(scale * q k^T) v for one sequence and head.
+
+    qi [Rq, D] are the query rows at local positions ``positions`` (Lq = lq),
+    ki / vi [Lk, D].  Two passes: row max over visible keys, then exp and sum.
+    Returns (out [Rq, D], lse [Rq]); rows that see no key give 0 and -inf.
+    """
+    lk = ki.shape[0]
+    rq = qi.shape[0]
+    out = np.zeros((rq, vi.shape[1]))
+    lse = np.full(rq, -np.inf)
+    if lk == 0 or rq == 0:
+        return out, lse
+    vis = _visibility(positions, lq, lk, causal)            # [Rq, Lk]
+    scores = scale * (qi @ ki.T)                              # [Rq, Lk]
+    live = vis.any(axis=1)                                    # rows seeing a key
+    m = np.where(vis, scores, -np.inf).max(axis=1)            # pass 1: row max
+    m_safe = np.where(live, m, 0.0)
+    w = np.where(vis, np.exp(scores - m_safe[:, None]), 0.0)  # pass 2: weights
+    den = w.sum(axis=1)
+    out[live] = (w[live] @ vi) / den[live, None]
+    lse[live] = m[live] + np.log(den[live])
+    return out, lse
+
+
+def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
+                     causal: bool = False, query_is_first_token: bool = False):
+    """Packed attention: every sequence attends only to itself.
+
+    q [rows_q, H, D], k/v [T_k, H, D] (float arrays or CPU tensors, widened to
+    float64).  Sequence i owns keys ``k[cu_k[i]:cu_k[i+1]]``; its queries are
+    ``q[cu_q[i]:cu_q[i+1]]``, or the single row ``q[i]`` (local position 0)
+    when ``query_is_first_token``.  ``scale`` is used as given (callers pass a
+    float32 value).  Returns (out [rows_q, H, D] float64, lse [H, rows_q]
+    float64).  Rows of q not owned by any sequence stay zero in ``out`` and
+    NaN in ``lse`` (the GPU never writes them).
+    """
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()] if cu_seqlens_q is not None else None
+    cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    num_seqs = len(cu_k) - 1
+    rows_q, heads, dim = q64.shape
+    out = np.zeros((rows_q, heads, v64.shape[2]))
+    lse = np.full((heads, rows_q), np.nan)
+    for i in range(num_seqs):
+        k0, k1 = cu_k[i], cu_k[i + 1]
+        lk = k1 - k0
+        if query_is_first_token:
+            rows = [i]
+            positions = [0]
+            lq = lk
+        else:
+            q0, q1 = cu_q[i], cu_q[i + 1]
+            rows = list(range(q0, q1))
+            positions = list(range(q1 - q0))
+            lq = q1 - q0
+        if not rows:
+            continue
+        for h in range(heads):
+            o, l = _attend_one(q64[rows, h, :], k64[k0:k1, h, :], v64[k0:k1, h, :],
+                               float(scale), causal, positions, lq)
+            out[rows, h, :] = o
+            lse[h, rows] = l
+    return out, lse
+
+
+def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
+                          causal: bool, samples):
+    """The same definition evaluated only at sampled (row, head) pairs.
+
+    For checks at full workload sizes, where the whole oracle would take too
+    long.  ``samples`` is a list of (packed query row, head); the row's
+    sequence is found by a linear scan of cu_seqlens_q.  Returns
+    (out [n, D] float64, lse [n] float64).
+    """
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    outs, lses = [], []
+    for row, h in samples:
+        seq = None
+        for i in range(len(cu_q) - 1):
+            if cu_q[i] <= row < cu_q[i + 1]:
+                seq = i
+                break
+        if seq is None:
+            raise ValueError(f"row {row} belongs to no sequence")
+        lq = cu_q[seq + 1] - cu_q[seq]
+        k0, k1 = cu_k[seq], cu_k[seq + 1]
+        o, l = _attend_one(q64[[row], h, :], k64[k0:k1, h, :], v64[k0:k1, h, :],
+                           float(scale), causal, [row - cu_q[seq]], lq)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.asarray(outs), np.asarray(lses)
