@@ -1,0 +1,347 @@
+"""Benchmark of the packed variable-length attention forward on one MI355X.
+
+One step = one pass of the whole path over one synthetic packed batch:
+  1. pack_sequences on the host (lengths -> cu_seqlens, flat_index) into a
+     pinned buffer, then an asynchronous copy of cu_seqlens to the device;
+  2. the device ragged-grid build (block_offsets, grid_mapping, tile_order);
+  3. the tiled attention forward (one launch of G_cap * heads workgroups).
+Q/K/V are resident in HBM before timing starts.  W warm-up steps, then K
+timed steps bracketed by synchronisation; the host work of step i overlaps the
+GPU work of step i-1.
+
+Also measured in the same run:
+  * the attention kernel alone, K launches timed with HIP events on the stream
+    it runs on (roofline "achieved");
+  * the padded comparator: torch SDPA over [B, H, L_max, D] on the same GPU
+    ("DanLing NestedTensor", Appendix C.8: padded attention is masked SDPA over
+    the padded envelope), inputs scattered before timing;
+  * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+
+Prints ONE JSON line.  Default workload: the Zipf decoder batch (64 sequences,
+Zipf s = 1 over 65,536 tokens, 16 heads x 128, causal, bf16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X datasheet
+HBM_PEAK_GBS = 8000.0
+METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 1 GPU"
+KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip", "tile_config.h",
+                  "attn_first_token.hip", "grid_build.hip"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "variable_length_packed_pack_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(lengths: np.ndarray, heads: int, head_dim: int, causal: bool) -> float:
+    """4 * sum N_i^2 * H * D, halved when causal."""
+    n2 = float(np.sum(lengths.astype(np.float64) ** 2))
+    f = 4.0 * n2 * heads * head_dim
+    return f / 2 if causal else f
+
+
+def compulsory_bytes(total: int, heads: int, head_dim: int, elt: int) -> float:
+    """q, k, v read once, out written once, lse written once."""
+    return 4.0 * total * heads * head_dim * elt + 4.0 * total * heads
+
+
+def traffic_from_profile(workload: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None
+    when no summary matches the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_oracle_baseline(wl, budget_s: float):
+    """Time the oracle on a bounded sample of the same batch: whole heads (every
+    sequence of the batch for that head), one after another, until the
+    elapsed time reaches the budget (at least one head)."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    cu = wl.cu_seqlens_host()
+    elapsed, heads_done = 0.0, 0
+    while heads_done < wl.heads and (heads_done == 0 or elapsed < budget_s):
+        hh = heads_done
+        q = wl.q[:, hh:hh + 1].float().numpy()
+        k = wl.k[:, hh:hh + 1].float().numpy()
+        v = wl.v[:, hh:hh + 1].float().numpy()
+        t0 = time.perf_counter()
+        oracle.varlen_attention(q, k, v, cu, cu, wl.scale, wl.causal)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+    flops = algorithmic_flops(wl.lengths, heads_done, wl.head_dim, wl.causal)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{heads_done} of {wl.heads} heads, all {wl.num_seqs} sequences "
+                   f"({flops / 1e9:.1f} GFLOP real-token), fp64 numpy, {elapsed:.1f} s"),
+        "seconds": elapsed,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+def padded_comparator(wl, q, k, v, reps: int):
+    """torch SDPA over the padded envelope [B, H, L_max, D] (same data),
+    chunked over the batch if the envelope is large; returns (ms, backend)."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    b, h, d = wl.num_seqs, wl.heads, wl.head_dim
+    lmax = wl.max_len
+    cu = wl.cu_seqlens_host()
+    elt = q.element_size()
+    per_seq = 4 * h * lmax * d * elt
+    chunk = max(1, min(b, int(40e9 // per_seq)))
+    total_ms = 0.0
+    backend_used = None
+    for c0 in range(0, b, chunk):
+        c1 = min(b, c0 + chunk)
+        nb = c1 - c0
+        qp = torch.zeros(nb, h, lmax, d, dtype=q.dtype, device=q.device)
+        kp = torch.zeros_like(qp)
+        vp = torch.zeros_like(qp)
+        for j, i in enumerate(range(c0, c1)):
+            s, e = int(cu[i]), int(cu[i + 1])
+            qp[j, :, : e - s] = q[s:e].transpose(0, 1)
+            kp[j, :, : e - s] = k[s:e].transpose(0, 1)
+            vp[j, :, : e - s] = v[s:e].transpose(0, 1)
+        mask = None
+        if not wl.causal:
+            lens = torch.as_tensor(wl.lengths[c0:c1], device=q.device)
+            mask = (torch.arange(lmax, device=q.device)[None, :] < lens[:, None])[:, None, None, :]
+        ran = None
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            if mask is not None and be == SDPBackend.FLASH_ATTENTION:
+                continue
+            try:
+                with sdpa_kernel([be]):
+                    torch.nn.functional.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask,
+                                                                     is_causal=wl.causal, scale=wl.scale)
+                torch.cuda.synchronize()
+                ran = be
+                break
+            except RuntimeError:
+                continue
+        if ran is None:
+            del qp, kp, vp
+            return None, "none (no fused SDPA backend accepted the envelope)"
+        backend_used = str(ran).split(".")[-1]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with sdpa_kernel([ran]):
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(reps):
+                torch.nn.functional.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, is_causal=wl.causal,
+                                                                 scale=wl.scale)
+            end.record()
+            torch.cuda.synchronize()
+        total_ms += start.elapsed_time(end) / reps
+        del qp, kp, vp
+        torch.cuda.empty_cache()
+    return total_ms, backend_used
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zipf", help="tiny | graph | encoder | zipf | skewed")
+    ap.add_argument("--no-padded", action="store_true", help="skip the padded SDPA comparator")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
+    ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward needs no exchange; see the design notes on sharding).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import variable_length_packed_pack_amd as vlp
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    vlp.load_library()
+    dev = torch.device("cuda:0")
+    k_idx = workloads.WORKLOAD_NAMES[args.workload]
+    log(f"[bench] generating workload {args.workload}")
+    wl = workloads.make_workload(k_idx)
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    t, h, d = wl.total_tokens, wl.heads, wl.head_dim
+    b = wl.num_seqs
+    flops = algorithmic_flops(wl.lengths, h, d, wl.causal)
+    out = torch.empty_like(q)
+    lse = torch.empty(h, t, dtype=torch.float32, device=dev)
+    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, False, b, t, wl.max_len)
+    ws = torch.empty(vlp.workspace_size(b, t, bm), dtype=torch.uint8, device=dev)
+    cu_dev = torch.empty(b + 1, dtype=torch.int32, device=dev)
+    lengths_host = wl.lengths.copy()
+    n_steps = args.warmup + args.steps
+    pinned = [torch.empty(b + 1, dtype=torch.int32).pin_memory() for _ in range(n_steps)]
+
+    def step(i: int) -> None:
+        flat, cu = vlp.pack_sequences(lengths_host, wl.max_len)
+        pinned[i].copy_(cu)
+        cu_dev.copy_(pinned[i], non_blocking=True)
+        vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+                            workspace=ws)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # host cost of pack_sequences alone (for the record)
+    tp = time.perf_counter()
+    for _ in range(20):
+        vlp.pack_sequences(lengths_host, wl.max_len)
+    pack_us = (time.perf_counter() - tp) * 1e6 / 20
+
+    # attention kernel alone: cached device grid, HIP events on the launch stream
+    cu_host = torch.from_numpy(wl.cu_seqlens_host())
+    grid_host = vlp.build_ragged_grid(cu_host, bm)
+    grid = vlp.RaggedGrid(grid_host.grid_mapping.to(dev), grid_host.block_offsets.to(dev),
+                          grid_host.tile_order.to(dev), grid_host.num_blocks, bm)
+    stream = torch.cuda.Stream(device=dev)
+    reps = args.kernel_only_reps or args.steps
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+                                grid=grid)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+                                grid=grid)
+        ev1.record(stream)
+    stream.synchronize()
+    kernel_ms = ev0.elapsed_time(ev1) / reps
+    torch.cuda.synchronize()
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(args.workload, src_hash)
+    elt = q.element_size()
+    log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
+
+    padded_ms, padded_backend = (None, "skipped")
+    if not args.no_padded:
+        log("[bench] padded SDPA comparator")
+        padded_ms, padded_backend = padded_comparator(wl, q, k, v, reps=3)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_oracle_baseline(wl, args.cpu_budget)
+
+    lmax = wl.max_len
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; no dataset)",
+        "config": {
+            "workload": wl.name,
+            "description": {
+                "zipf": "64 sequences, Zipf (s=1) lengths over 65,536 tokens, 16 heads x 128, causal, bf16",
+                "skewed": "255 x U[64,256] + one 32,768-token sequence, 32 heads x 128, causal, bf16",
+                "encoder": "128 sequences, gamma(2,75) lengths clipped to [8,384], 12 heads x 64, bf16",
+                "graph": "512 sequences, lognormal(ln 80, 0.6) lengths clipped to [1,256], 8 heads x 64, fp32",
+                "tiny": "8 sequences, U[1,64] lengths, 2 heads x 16, fp32",
+            }[wl.name],
+            "num_seqs": b,
+            "total_tokens": t,
+            "max_seqlen": lmax,
+            "heads": h,
+            "head_dim": d,
+            "causal": wl.causal,
+            "block_m": bm,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
+        "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
+        "padded_ms": None if padded_ms is None else round(padded_ms, 3),
+        "padded_backend": padded_backend,
+        "kernel_ms": round(kernel_ms, 4),
+        "kernel_source_hash": src_hash,
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "compulsory_gb": round(compulsory_bytes(t, h, d, elt) / 1e9, 4),
+        "rho_seq": round(t / (b * lmax), 4),
+        "work_ratio": round(float(np.sum(wl.lengths.astype(np.float64) ** 2)) / (b * lmax * lmax), 5),
+        "pack_sequences_host_us": round(pack_us, 1),
+        "cpu_baseline_detail": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

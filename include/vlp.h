@@ -1,0 +1,263 @@
+/*
+ * vlp.h -- packed variable-length attention forward for AMD Instinct MI355X
+ * (gfx950): the C ABI of libvlp.so.
+ *
+ * The operation: a batch of B sequences is packed token-major into one buffer
+ * [num_tokens, heads, head_dim]; sequence i occupies rows
+ * [cu_seqlens[i], cu_seqlens[i+1]) and attends only to itself.  Sources:
+ *   - "gigl.nn.packed_attention": the module description ("each sequence
+ *     attends only to itself, with boundaries given by cu_seqlens"), "Data
+ *     flow of a packed forward", "Constraints", "Example", and the
+ *     packed_attention entry (query_is_first_token).
+ *   - "PyCoRa: A PyTorch implementation of CoRa Ragged Tensors": "The Data
+ *     Structure", "CoRa Metadata" (grid_mapping, block_offsets) and "Ragged
+ *     Flash Attention" (tiled online softmax routed through grid_mapping).
+ *   - "So you wanna CUDA Graph" (attention-gym): "What are ragged kernels?"
+ *     (the cu_seqlens convention), "Terminology time" (capacity tails),
+ *     "Scheduling without max_seqlen" (flat tile list, its decode and the
+ *     launch capacity G_cap), "Correctness tangent" (inactive rows).
+ *   - "DanLing NestedTensor", section 3.3 "Attention through packed blocks"
+ *     (token-major q/k/v, separate query and key boundaries).
+ *
+ * Conventions shared by every entry point:
+ *   - All functions are non-throwing and reentrant and keep no pointer after
+ *     they return.  The caller owns every buffer.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory on the current device.
+ *   - Device entry points only enqueue work on `stream` (a hipStream_t passed
+ *     as void*, NULL = the null stream); they never synchronise and never read
+ *     device memory on the host, so the values in device buffers (cu_seqlens
+ *     in particular) are NOT validated: out-of-contract values give undefined
+ *     output.  Every argument the host can see is validated before any HIP
+ *     call, and a failed check returns a status without touching the GPU.
+ */
+#ifndef VLP_H_
+#define VLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vlp_status;
+
+enum {
+  VLP_OK = 0,
+  VLP_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  VLP_ERR_INVALID = 2,     /* an argument value is out of contract         */
+  VLP_ERR_UNSUPPORTED = 3, /* dtype / head_dim / mode not built            */
+  VLP_ERR_CAPACITY = 4,    /* an output or workspace buffer is too small   */
+  VLP_ERR_OVERFLOW = 5,    /* a count does not fit in int32                */
+  VLP_ERR_HIP = 6          /* a HIP runtime call failed (kernel launch)    */
+};
+
+/* Element types of q, k, v and out. */
+enum { VLP_FP32 = 0, VLP_FP16 = 1, VLP_BF16 = 2 };
+
+/*
+ * vlp_pack_sequences -- lengths -> flat_index, cu_seqlens (all host memory).
+ *
+ * "gigl.nn.packed_attention", "Data flow of a packed forward" and "Example":
+ * cu_seqlens[0] = 0, cu_seqlens[i+1] = cu_seqlens[i] + lengths[i]; the packed
+ * buffer is padded_grid.flatten()[flat_index], where flat_index lists the
+ * row-major positions i*max_seq_len + j (j < lengths[i]) of the real tokens of
+ * the padded grid [num_seqs, max_seq_len], sequence after sequence.
+ * Example: lengths {3,1,2}, max_seq_len 3 -> flat_index {0,1,2,3,6,7},
+ * cu_seqlens {0,3,4,6}.
+ *
+ *   lengths      host int32 [num_seqs]; each in [1, max_seq_len]
+ *                ("Every sequence must contain at least one token").
+ *   num_seqs     >= 1.
+ *   max_seq_len  >= 1, the padded grid's row length.
+ *   flat_index   host int64 [flat_index_cap], or NULL to query the size only.
+ *   cu_seqlens   host int32 [num_seqs + 1], always written on success and on
+ *                VLP_ERR_CAPACITY.
+ *   num_tokens   host int64*, receives sum(lengths) (the one host-visible
+ *                count the packing needs).
+ * Errors: NULL lengths / cu_seqlens / num_tokens -> VLP_ERR_NULL; num_seqs < 1,
+ * max_seq_len < 1, a length < 1 or > max_seq_len -> VLP_ERR_INVALID; total >
+ * INT32_MAX ("cu_seqlens is int32, so the token count must fit in int32") ->
+ * VLP_ERR_OVERFLOW; flat_index != NULL and flat_index_cap < total ->
+ * VLP_ERR_CAPACITY (cu_seqlens and num_tokens still filled in).
+ */
+vlp_status vlp_pack_sequences(const int32_t* lengths, int32_t num_seqs, int32_t max_seq_len,
+                              int64_t* flat_index, int64_t flat_index_cap,
+                              int32_t* cu_seqlens, int64_t* num_tokens);
+
+/*
+ * vlp_grid_capacity -- G_cap(T, N, C) = M + floor((T - M) / C), M = min(T, N).
+ *
+ * "So you wanna CUDA Graph", "Scheduling without max_seqlen": an upper bound
+ * on the number of active tiles for any split of at most T tokens over at
+ * most N sequences, usable as a launch size without reading cu_seqlens.
+ * Returns -1 if total_tokens < 0, num_seqs < 0 or block_m < 1.
+ */
+int64_t vlp_grid_capacity(int64_t total_tokens, int32_t num_seqs, int32_t block_m);
+
+/*
+ * vlp_build_ragged_grid -- CoRa-style tile metadata on the host.
+ *
+ * "PyCoRa", "CoRa Metadata" and "So you wanna CUDA Graph", "Scheduling
+ * without max_seqlen":
+ *   block_offsets[0] = 0, block_offsets[i+1] = block_offsets[i]
+ *       + ceil(len_i / block_m), len_i = cu_seqlens[i+1] - cu_seqlens[i]
+ *       (the ceiling restarts at every sequence; block_offsets[B] = G, the
+ *       number of active tiles);
+ *   grid_mapping[f] = the sequence i with block_offsets[i] <= f <
+ *       block_offsets[i+1] (zero-length sequences own no tile);
+ *   tile_order[s] = the flat tile run by the s-th launched tile slot, longest
+ *       sequence first: sequences by length descending (ties: lower index
+ *       first), each with its tiles from the last local tile down to tile 0.
+ *
+ *   cu_seqlens     host int32 [num_seqs + 1]: cu[0] == 0, non-decreasing.
+ *   block_offsets  host int32 [num_seqs + 1].
+ *   grid_mapping, tile_order  host int32 [grid_cap] (either may be NULL to
+ *                  skip it).
+ *   num_blocks     host int64*, receives G.
+ * Errors: NULL cu_seqlens / block_offsets / num_blocks -> VLP_ERR_NULL;
+ * num_seqs < 1, block_m < 1, cu[0] != 0 or decreasing cu -> VLP_ERR_INVALID;
+ * G > grid_cap -> VLP_ERR_CAPACITY (block_offsets and num_blocks filled in).
+ */
+vlp_status vlp_build_ragged_grid(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
+                                 int32_t* block_offsets, int32_t* grid_mapping,
+                                 int32_t* tile_order, int64_t grid_cap, int64_t* num_blocks);
+
+/*
+ * vlp_build_ragged_grid_device -- the same metadata, built on the GPU from a
+ * device cu_seqlens without any host read (one workgroup, enqueued on
+ * `stream`).  Bit-identical to vlp_build_ragged_grid whenever num_seqs <=
+ * VLP_DEVICE_SORT_MAX_SEQS; above that the device tile_order is the natural
+ * order 0..G-1 (block_offsets and grid_mapping are unaffected).
+ *
+ *   cu_seqlens     device int32 [num_seqs + 1].
+ *   block_offsets  device int32 [num_seqs + 1].
+ *   grid_mapping, tile_order  device int32 [grid_cap]; entries >= G are set
+ *                  to -1.
+ *   grid_cap       must be >= G; pass vlp_grid_capacity(T, num_seqs, block_m)
+ *                  with T >= cu_seqlens[num_seqs] to be safe.  Tiles beyond
+ *                  grid_cap are dropped (undefined metadata), not detected.
+ * Errors: NULL pointers -> VLP_ERR_NULL; num_seqs < 1, block_m < 1, grid_cap <
+ * 0 -> VLP_ERR_INVALID; launch failure -> VLP_ERR_HIP.
+ */
+#define VLP_DEVICE_SORT_MAX_SEQS 4096
+vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
+                                        int32_t* block_offsets, int32_t* grid_mapping,
+                                        int32_t* tile_order, int64_t grid_cap, void* stream);
+
+/*
+ * vlp_kernel_block_m -- the query rows per tile (the C of the ragged grid)
+ * that vlp_varlen_attn_fwd uses for these arguments, or -1 if the combination
+ * is unsupported.  A grid passed to vlp_varlen_attn_fwd_grid must be built
+ * with this block_m.  In first-token mode every sequence is one tile, and the
+ * value returned is VLP_FIRST_TOKEN_BLOCK_M (a grid over cu_seqlens_k with
+ * this block_m has exactly one tile per non-empty sequence).
+ *   max_seqlen  a hint (0 = unknown); the choice never affects correctness.
+ */
+#define VLP_FIRST_TOKEN_BLOCK_M (1 << 30)
+int32_t vlp_kernel_block_m(int32_t dtype, int32_t head_dim, int32_t causal,
+                           int32_t query_is_first_token, int32_t num_seqs,
+                           int64_t rows_q, int32_t max_seqlen);
+
+/*
+ * vlp_varlen_attn_workspace_size -- bytes of device workspace that
+ * vlp_varlen_attn_fwd needs for the device-built grid (block_offsets,
+ * grid_mapping, tile_order for G_cap(rows, num_seqs, block_m) tiles, where
+ * rows = rows_q, or num_seqs in first-token mode).
+ * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, block_m < 1
+ * -> VLP_ERR_INVALID.
+ */
+vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int32_t block_m,
+                                          size_t* bytes);
+
+/*
+ * vlp_varlen_attn_fwd -- packed attention forward, out = softmax(scale q k^T) v
+ * within each sequence, plus the log-sum-exp of every query row.
+ *
+ * "gigl.nn.packed_attention" (packed_attention; "Example"), "PyCoRa" ("Ragged
+ * Flash Attention"), "DanLing NestedTensor" 3.3 ("Attention through packed
+ * blocks": the output takes the query structure; query and key lengths may
+ * differ).  Enqueues, on `stream`, the device grid build into `workspace`
+ * (no host read of cu_seqlens) and one attention launch of
+ * G_cap * heads workgroups in which surplus tiles exit at once.
+ *
+ *   dtype          VLP_FP32, VLP_FP16 or VLP_BF16 for q, k, v and out; the
+ *                  contractions accumulate in fp32, the softmax runs in fp32.
+ *   q              device [rows_q, heads, head_dim], contiguous; in
+ *                  first-token mode rows_q == num_seqs and row i is the query
+ *                  of sequence i (the page's query[cu_seqlens[:-1]]).
+ *   k, v           device [total_k, heads, head_dim], contiguous.
+ *   cu_seqlens_q   device int32 [num_seqs + 1] (ignored, may be NULL, in
+ *                  first-token mode).
+ *   cu_seqlens_k   device int32 [num_seqs + 1]; cu[0] = 0, non-decreasing,
+ *                  cu[B] <= total_k.  Zero-length sequences are allowed
+ *                  (capacity tails [0, .., L, L, L]) except in first-token
+ *                  mode, where every sequence needs a key.
+ *   num_seqs       B >= 1.
+ *   rows_q         physical query rows (>= cu_seqlens_q[B]); rows not owned
+ *                  by a sequence are never written.
+ *   total_k        physical key rows.
+ *   heads, head_dim  heads >= 1; head_dim in {16, 32, 64, 128} ("head_dim must
+ *                  be a multiple of 8"; these four are built).
+ *   max_seqlen     a hint (0 = unknown); never needed for correctness.
+ *   scale          finite softmax scale (usually 1/sqrt(head_dim)).
+ *   causal         0/1: key j of a sequence is visible to its query at local
+ *                  position p iff j <= p + (Lk - Lq) (bottom-right aligned).
+ *   query_is_first_token  0/1: one query per sequence, at local position 0.
+ *   out            device [rows_q, heads, head_dim] in dtype.
+ *   lse            device fp32 [heads, rows_q] or NULL: natural-log
+ *                  log-sum-exp of the scaled scores; -inf (and a zero output
+ *                  row) for a query that sees no key.
+ *   workspace      device, >= vlp_varlen_attn_workspace_size bytes, 256-byte
+ *                  aligned; overwritten.
+ * q, k, v and out must be 16-byte aligned.
+ * Errors: NULL q/k/v/out/cu_seqlens_k/workspace (or cu_seqlens_q outside
+ * first-token mode) -> VLP_ERR_NULL; dtype or head_dim not built ->
+ * VLP_ERR_UNSUPPORTED; num_seqs < 1, heads < 1, rows_q < 0, total_k < 0,
+ * non-finite scale, misaligned pointers, rows_q != num_seqs in first-token
+ * mode -> VLP_ERR_INVALID; rows or rows*heads beyond int32 -> VLP_ERR_OVERFLOW;
+ * small workspace -> VLP_ERR_CAPACITY; launch failure -> VLP_ERR_HIP.
+ */
+vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                               int32_t heads, int32_t head_dim, int32_t max_seqlen,
+                               float scale, int32_t causal, int32_t query_is_first_token,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * vlp_varlen_attn_fwd_grid -- the same forward with caller-supplied, cached
+ * tile metadata ("PyCoRa", "CoRa Metadata": computed once and cached).
+ *
+ *   grid_mapping, block_offsets, tile_order  device int32, as produced by
+ *                  vlp_build_ragged_grid(_device) for cu_seqlens_q (or, in
+ *                  first-token mode, cu_seqlens_k) with `block_m`.
+ *   tile_order     may be NULL: flat tiles then run in natural order.
+ *   num_blocks     G, the number of active tiles; exactly G * heads
+ *                  workgroups are launched.
+ *   block_m        must equal vlp_kernel_block_m(...) for these arguments.
+ * Errors: as vlp_varlen_attn_fwd (workspace not used), plus NULL grid_mapping
+ * / block_offsets -> VLP_ERR_NULL, num_blocks < 0 or a block_m mismatch ->
+ * VLP_ERR_INVALID, num_blocks * heads beyond int32 -> VLP_ERR_OVERFLOW.
+ */
+vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                    int32_t heads, int32_t head_dim, int32_t max_seqlen,
+                                    float scale, int32_t causal, int32_t query_is_first_token,
+                                    void* out, float* lse,
+                                    const int32_t* grid_mapping, const int32_t* block_offsets,
+                                    const int32_t* tile_order, int64_t num_blocks, int32_t block_m,
+                                    void* stream);
+
+/* vlp_status_string -- a static, human-readable name for a status code; for
+ * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */
+const char* vlp_status_string(vlp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLP_H_ */

@@ -254,10 +254,10 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
 
     For checks at full workload sizes, where the whole oracle would take too
     long.  ``samples`` is a list of (packed query row, head); the row's
-    sequence is found by a linear scan of cu_seqlens_q.  Returns
-    (out [n, D] float64, lse [n] float64).
+    sequence is found by a linear scan of cu_seqlens_q.  Only the slices a
+    sample needs are widened to float64.  Returns (out [n, D] float64,
+    lse [n] float64).
     """
-    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
     cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
     cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
     outs, lses = [], []
@@ -271,8 +271,10 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
             raise ValueError(f"row {row} belongs to no sequence")
         lq = cu_q[seq + 1] - cu_q[seq]
         k0, k1 = cu_k[seq], cu_k[seq + 1]
-        o, l = _attend_one(q64[[row], h, :], k64[k0:k1, h, :], v64[k0:k1, h, :],
-                           float(scale), causal, [row - cu_q[seq]], lq)
+        qi = _as_f64(q[row:row + 1, h, :])
+        ki = _as_f64(k[k0:k1, h, :])
+        vi = _as_f64(v[k0:k1, h, :])
+        o, l = _attend_one(qi, ki, vi, float(scale), causal, [row - cu_q[seq]], lq)
         outs.append(o[0])
         lses.append(l[0])
     return np.asarray(outs), np.asarray(lses)

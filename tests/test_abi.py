@@ -1,0 +1,275 @@
+"""CPU tier: the C ABI loads, exports what include/vlp.h declares, and its host
+functions agree bit for bit with the oracle.  Argument validation of the
+device entry points is exercised with dummy pointers: every case here fails
+on the host before any HIP call, so no GPU is needed.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_packed_pack_amd as vlp
+from variable_length_packed_pack_amd import _lib
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vlp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libvlp.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vlp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for must in ("vlp_pack_sequences", "vlp_build_ragged_grid", "vlp_varlen_attn_fwd",
+                 "vlp_varlen_attn_fwd_grid", "vlp_build_ragged_grid_device", "vlp_grid_capacity",
+                 "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert f"#define VLP_DEVICE_SORT_MAX_SEQS {_lib.VLP_DEVICE_SORT_MAX_SEQS}" in text
+    assert "#define VLP_FIRST_TOKEN_BLOCK_M (1 << 30)" in text
+    for name in ("VLP_FP32 = 0", "VLP_FP16 = 1", "VLP_BF16 = 2", "VLP_OK = 0", "VLP_ERR_HIP = 6"):
+        assert name in text
+
+
+# --------------------------------------------------------------------------
+# pack_sequences
+# --------------------------------------------------------------------------
+
+def test_pack_worked_example():
+    flat, cu = vlp.pack_sequences([3, 1, 2], 3)
+    assert flat.tolist() == [0, 1, 2, 3, 6, 7]
+    assert cu.tolist() == [0, 3, 4, 6]
+    assert flat.dtype == torch.int64 and cu.dtype == torch.int32
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_pack_matches_oracle_on_workloads(k):
+    lengths = workloads.draw_lengths(k)
+    max_len = int(lengths.max())
+    flat, cu = vlp.pack_sequences(lengths, max_len)
+    oflat, ocu = oracle.pack_sequences(lengths, max_len)
+    assert np.array_equal(flat.numpy(), oflat)
+    assert np.array_equal(cu.numpy(), ocu)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_pack_fuzz_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 200))
+    max_len = int(rng.integers(1, 500))
+    lengths = rng.integers(1, max_len + 1, size=b)
+    flat, cu = vlp.pack_sequences(lengths, max_len)
+    oflat, ocu = oracle.pack_sequences(lengths, max_len)
+    assert np.array_equal(flat.numpy(), oflat) and np.array_equal(cu.numpy(), ocu)
+
+
+def test_pack_errors():
+    lib = _lib.load()
+    lens = np.asarray([3, 0, 2], dtype=np.int32)
+    cu = np.zeros(4, dtype=np.int32)
+    tot = ctypes.c_int64(0)
+    assert lib.vlp_pack_sequences(lens.ctypes.data, 3, 3, None, 0, cu.ctypes.data, ctypes.addressof(tot)) == 2
+    lens = np.asarray([3, 4], dtype=np.int32)
+    assert lib.vlp_pack_sequences(lens.ctypes.data, 2, 3, None, 0, cu.ctypes.data, ctypes.addressof(tot)) == 2
+    assert lib.vlp_pack_sequences(None, 2, 3, None, 0, cu.ctypes.data, ctypes.addressof(tot)) == 1
+    assert lib.vlp_pack_sequences(lens.ctypes.data, 0, 3, None, 0, cu.ctypes.data, ctypes.addressof(tot)) == 2
+    big = np.asarray([2**30 + 1, 2**30 + 1], dtype=np.int32)
+    assert lib.vlp_pack_sequences(big.ctypes.data, 2, 2**30 + 1, None, 0, cu.ctypes.data,
+                                  ctypes.addressof(tot)) == 5
+    lens = np.asarray([3, 1, 2], dtype=np.int32)
+    flat = np.zeros(5, dtype=np.int64)
+    st = lib.vlp_pack_sequences(lens.ctypes.data, 3, 3, flat.ctypes.data, 5, cu.ctypes.data, ctypes.addressof(tot))
+    assert st == 4 and tot.value == 6 and cu.tolist() == [0, 3, 4, 6]
+    with pytest.raises(vlp.VlpError):
+        vlp.pack_sequences([1, 0], 4)
+
+
+# --------------------------------------------------------------------------
+# ragged grid (host)
+# --------------------------------------------------------------------------
+
+def test_grid_worked_example():
+    g = vlp.build_ragged_grid(torch.tensor([0, 65, 128], dtype=torch.int32), 64)
+    assert g.block_offsets.tolist() == [0, 2, 3]
+    assert g.grid_mapping.tolist() == [0, 0, 1]
+    assert g.tile_order.tolist() == [1, 0, 2]
+    assert g.num_blocks == 3
+
+
+def _cu(lengths):
+    return torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+
+
+@pytest.mark.parametrize("block_m", [1, 7, 32, 64, 128, 1 << 30])
+@pytest.mark.parametrize("seed", range(6))
+def test_grid_matches_oracle(seed, block_m):
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 300))
+    lengths = rng.integers(0 if seed % 2 else 1, 700, size=b)
+    if seed % 3 == 0:
+        lengths[rng.integers(0, b, size=b // 3)] = 64  # many ties
+    cu = _cu(lengths)
+    g = vlp.build_ragged_grid(cu, block_m)
+    bo, gm, to = oracle.build_ragged_grid(cu.numpy(), block_m)
+    assert np.array_equal(g.block_offsets.numpy(), bo)
+    assert np.array_equal(g.grid_mapping.numpy(), gm)
+    assert np.array_equal(g.tile_order.numpy(), to)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_grid_matches_oracle_on_workloads(k):
+    lengths = workloads.draw_lengths(k)
+    cu = _cu(lengths)
+    for bm in (32, 64, 128):
+        g = vlp.build_ragged_grid(cu, bm)
+        bo, gm, to = oracle.build_ragged_grid(cu.numpy(), bm)
+        assert np.array_equal(g.block_offsets.numpy(), bo)
+        assert np.array_equal(g.grid_mapping.numpy(), gm)
+        assert np.array_equal(g.tile_order.numpy(), to)
+
+
+def test_grid_capacity_matches_oracle():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        t = int(rng.integers(0, 10**6))
+        n = int(rng.integers(0, 5000))
+        c = int(rng.integers(1, 300))
+        assert vlp.grid_capacity(t, n, c) == oracle.grid_capacity(t, n, c)
+    assert vlp.grid_capacity(-1, 3, 4) == -1 and vlp.grid_capacity(3, 3, 0) == -1
+
+
+def test_grid_errors():
+    lib = _lib.load()
+    bo = np.zeros(3, dtype=np.int32)
+    gm = np.zeros(8, dtype=np.int32)
+    nb = ctypes.c_int64(0)
+    bad = np.asarray([1, 65, 128], dtype=np.int32)
+    assert lib.vlp_build_ragged_grid(bad.ctypes.data, 2, 64, bo.ctypes.data, None, None, 0,
+                                     ctypes.addressof(nb)) == 2
+    dec = np.asarray([0, 65, 60], dtype=np.int32)
+    assert lib.vlp_build_ragged_grid(dec.ctypes.data, 2, 64, bo.ctypes.data, None, None, 0,
+                                     ctypes.addressof(nb)) == 2
+    ok = np.asarray([0, 65, 128], dtype=np.int32)
+    assert lib.vlp_build_ragged_grid(ok.ctypes.data, 2, 0, bo.ctypes.data, None, None, 0,
+                                     ctypes.addressof(nb)) == 2
+    st = lib.vlp_build_ragged_grid(ok.ctypes.data, 2, 64, bo.ctypes.data, gm.ctypes.data, None, 2,
+                                   ctypes.addressof(nb))
+    assert st == 4 and nb.value == 3 and bo.tolist() == [0, 2, 3]
+    assert lib.vlp_build_ragged_grid(None, 2, 64, bo.ctypes.data, None, None, 0, ctypes.addressof(nb)) == 1
+
+
+def test_kernel_block_m_and_workspace():
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        for d in (16, 32, 64, 128):
+            bm = vlp.kernel_block_m(dt, d)
+            assert bm >= 32 and bm % 32 == 0
+            assert vlp.kernel_block_m(dt, d, query_is_first_token=True) == vlp.VLP_FIRST_TOKEN_BLOCK_M
+        assert vlp.kernel_block_m(dt, 48) == -1
+        assert vlp.kernel_block_m(dt, 256) == -1
+    assert vlp.kernel_block_m(torch.int32, 64) == -1
+    ws = vlp.workspace_size(64, 65536, 128)
+    cap = vlp.grid_capacity(65536, 64, 128)
+    assert ws >= 4 * (65 + 2 * cap)
+
+
+# --------------------------------------------------------------------------
+# forward argument validation (host only; no HIP call is reached)
+# --------------------------------------------------------------------------
+
+FAKE = 0x10000  # aligned, never dereferenced: each case fails validation first
+
+
+def _fwd(**kw):
+    lib = _lib.load()
+    a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100, total_k=100, heads=2,
+             head_dim=64, max_seqlen=0, scale=0.125, causal=0, ft=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.vlp_varlen_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["b"], a["rows_q"],
+                                   a["total_k"], a["heads"], a["head_dim"], a["max_seqlen"], a["scale"],
+                                   a["causal"], a["ft"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_forward_validation_errors():
+    assert _fwd(q=None) == 1
+    assert _fwd(cu_k=None) == 1
+    assert _fwd(cu_q=None) == 1
+    assert _fwd(ws=None) == 1
+    assert _fwd(dtype=7) == 3
+    assert _fwd(head_dim=48) == 3
+    assert _fwd(head_dim=256) == 3
+    assert _fwd(b=0) == 2
+    assert _fwd(heads=0) == 2
+    assert _fwd(rows_q=-1) == 2
+    assert _fwd(scale=float("nan")) == 2
+    assert _fwd(scale=float("inf")) == 2
+    assert _fwd(q=FAKE + 8) == 2
+    assert _fwd(out=FAKE + 4) == 2
+    assert _fwd(ws=FAKE + 16) == 2
+    assert _fwd(causal=2) == 2
+    assert _fwd(ft=1, rows_q=100) == 2          # first-token: one query per sequence
+    assert _fwd(rows_q=2**31) == 5
+    assert _fwd(rows_q=2**30, heads=4) == 5
+    assert _fwd(ws_bytes=16) == 4
+
+
+def test_grid_forward_validation_errors():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(gm=FAKE, bo=FAKE, to=None, nb=3, bm=128, head_dim=128)
+        a.update(kw)
+        return lib.vlp_varlen_attn_fwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, a["head_dim"], 0,
+                                            0.1, 0, 0, FAKE, None, a["gm"], a["bo"], a["to"], a["nb"], a["bm"],
+                                            None)
+    assert call(gm=None) == 1
+    assert call(bo=None) == 1
+    assert call(nb=-1) == 2
+    assert call(bm=64) == 2                      # must equal vlp_kernel_block_m
+    assert call(nb=2**31) == 5
+
+
+def test_device_grid_validation_errors():
+    lib = _lib.load()
+    assert lib.vlp_build_ragged_grid_device(None, 2, 64, FAKE, FAKE, FAKE, 4, None) == 1
+    assert lib.vlp_build_ragged_grid_device(FAKE, 0, 64, FAKE, FAKE, FAKE, 4, None) == 2
+    assert lib.vlp_build_ragged_grid_device(FAKE, 2, 0, FAKE, FAKE, FAKE, 4, None) == 2
+    assert lib.vlp_build_ragged_grid_device(FAKE, 2, 64, FAKE, FAKE, FAKE, -1, None) == 2
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(7):
+        assert lib.vlp_status_string(code)
+    assert b"unknown" in lib.vlp_status_string(99)
+
+
+def test_sources_never_bit_cast_a_vector_subscript():
+    """hipcc (clang 22, ROCm 7.2) reads element 0 when __builtin_bit_cast is
+    applied directly to an ext_vector_type subscript such as v[i]; the
+    kernels bit-cast whole vectors instead.  Keep the pattern out."""
+    csrc = os.path.join(ROOT, "variable_length_packed_pack_amd", "csrc")
+    pat = re.compile(r"__builtin_bit_cast\s*\([^,()]+,\s*[A-Za-z_]\w*\s*\[")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        assert not pat.search(text), name

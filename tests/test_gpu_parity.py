@@ -1,0 +1,364 @@
+"""GPU tier: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances: out max-abs 1e-4 for fp32 and 2e-2 for bf16/fp16, lse 1e-3, the
+oracle running in float64 on the same rounded inputs; metadata bit-exact.
+Workloads 1-3 are checked on every row; 4 and 5 (full size, in the launch
+configuration the benchmark times) on sampled rows that the oracle computes
+one by one, plus properties of every row.
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_packed_pack_amd as vlp
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 2e-2}
+TOL_LSE = 1e-3
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vlp.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cu(lengths):
+    return torch.from_numpy(np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32))
+
+
+def _to_dev(wl):
+    cu = torch.from_numpy(wl.cu_seqlens_host())
+    return wl.q.to(DEV), wl.k.to(DEV), wl.v.to(DEV), cu.to(DEV), cu
+
+
+def _gpu_forward(wl, causal=None, first_token=False, grid=None):
+    q, k, v, cu_d, cu_h = _to_dev(wl)
+    causal = wl.causal if causal is None else causal
+    if first_token:
+        q = q[cu_h[:-1].long()].contiguous()
+    out, lse = vlp.varlen_attn_fwd(q, k, v, None if first_token else cu_d, cu_d, wl.max_len, wl.scale, causal,
+                                   first_token, grid=grid)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check_full(wl, causal=None, first_token=False):
+    causal = wl.causal if causal is None else causal
+    _say(f"[parity] {wl.name} dtype={wl.dtype} B={wl.num_seqs} T={wl.total_tokens} H={wl.heads} "
+         f"D={wl.head_dim} causal={causal} first_token={first_token}")
+    out, lse = _gpu_forward(wl, causal, first_token)
+    cu = wl.cu_seqlens_host()
+    q = wl.q[torch.from_numpy(cu[:-1]).long()] if first_token else wl.q
+    ref, ref_lse = oracle.varlen_attention(q, wl.k, wl.v, None if first_token else cu, cu, wl.scale, causal,
+                                           query_is_first_token=first_token)
+    err = np.max(np.abs(out.float().cpu().numpy().astype(np.float64) - ref))
+    lerr = np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse))
+    _say(f"[parity]   out max-abs {err:.3e}  lse max-abs {lerr:.3e}")
+    assert err <= TOL_OUT[wl.dtype], err
+    assert lerr <= TOL_LSE, lerr
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# metadata on the device
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("block_m", [32, 64, 128, vlp.VLP_FIRST_TOKEN_BLOCK_M])
+def test_device_grid_bit_exact(k, block_m):
+    lengths = workloads.draw_lengths(k)
+    cu = _cu(lengths)
+    cap = vlp.grid_capacity(int(cu[-1]), len(lengths), block_m)
+    g = vlp.build_ragged_grid(cu.to(DEV), block_m, grid_cap=cap)
+    bo, gm, to = oracle.build_ragged_grid(cu.numpy(), block_m)
+    n = len(gm)
+    assert np.array_equal(g.block_offsets.cpu().numpy(), bo)
+    assert np.array_equal(g.grid_mapping.cpu().numpy()[:n], gm)
+    assert np.array_equal(g.tile_order.cpu().numpy()[:n], to)
+    assert np.all(g.grid_mapping.cpu().numpy()[n:] == -1) and np.all(g.tile_order.cpu().numpy()[n:] == -1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_device_grid_fuzz_with_ties_and_empty_tails(seed):
+    rng = np.random.default_rng(seed)
+    b = int(rng.integers(1, 3000))
+    lengths = rng.integers(0, 400, size=b)
+    lengths[rng.integers(0, b, size=b // 2)] = 128
+    if b > 3:
+        lengths[-3:] = 0
+    cu = _cu(lengths)
+    for bm in (64, 128):
+        cap = vlp.grid_capacity(int(cu[-1]) + 17, b, bm)
+        g = vlp.build_ragged_grid(cu.to(DEV), bm, grid_cap=cap)
+        bo, gm, to = oracle.build_ragged_grid(cu.numpy(), bm)
+        assert np.array_equal(g.block_offsets.cpu().numpy(), bo)
+        assert np.array_equal(g.grid_mapping.cpu().numpy()[:len(gm)], gm)
+        assert np.array_equal(g.tile_order.cpu().numpy()[:len(to)], to)
+
+
+def test_device_grid_natural_order_beyond_sort_limit():
+    rng = np.random.default_rng(9)
+    b = vlp.VLP_DEVICE_SORT_MAX_SEQS + 5
+    lengths = rng.integers(0, 50, size=b)
+    cu = _cu(lengths)
+    cap = vlp.grid_capacity(int(cu[-1]), b, 64)
+    g = vlp.build_ragged_grid(cu.to(DEV), 64, grid_cap=cap)
+    bo, gm, _ = oracle.build_ragged_grid(cu.numpy(), 64)
+    assert np.array_equal(g.block_offsets.cpu().numpy(), bo)
+    assert np.array_equal(g.grid_mapping.cpu().numpy()[:len(gm)], gm)
+    assert np.array_equal(g.tile_order.cpu().numpy()[:len(gm)], np.arange(len(gm)))
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+def test_workload_tiny_fp32():
+    wl = workloads.make_workload(1)
+    _check_full(wl)
+    _check_full(wl, causal=True)
+    _check_full(wl, first_token=True)
+
+
+def test_pack_example_shapes_on_gpu():
+    flat, cu = vlp.pack_sequences([3, 1, 2], 3)
+    wl = workloads.custom_workload([3, 1, 2], 2, 8 * 2, "fp32", False, seed=5)
+    out, _ = _gpu_forward(wl)
+    assert list(out.shape) == [6, 2, 16]
+    first, _ = _gpu_forward(wl, first_token=True)
+    assert list(first.shape) == [3, 2, 16]
+    assert flat.tolist() == [0, 1, 2, 3, 6, 7] and cu.tolist() == [0, 3, 4, 6]
+
+
+def test_workload_graph_fp32():
+    wl = workloads.make_workload(2)
+    out, lse = _check_full(wl)
+    first, lse_first = _check_full(wl, first_token=True)
+    cu = wl.cu_seqlens_host()
+    rows = torch.from_numpy(cu[:-1]).long().to(DEV)
+    # first-token rows equal the full forward's rows cu[:-1] ("Data flow": anchor readout)
+    assert (first - out[rows]).abs().max().item() <= 2 * TOL_OUT["fp32"]
+    assert (lse_first - lse[:, rows]).abs().max().item() <= 2 * TOL_LSE
+
+
+def test_workload_encoder_bf16():
+    wl = workloads.make_workload(3)
+    _check_full(wl)
+
+
+def test_workload_encoder_fp16():
+    wl = workloads.make_workload(3, dtype_override="fp16")
+    _check_full(wl)
+
+
+def _sample_rows(wl, rng, count):
+    cu = wl.cu_seqlens_host()
+    lengths = wl.lengths
+    longest = int(np.argmax(lengths))
+    picks = set()
+    a, b = int(cu[longest]), int(cu[longest + 1])
+    bm = vlp.kernel_block_m(workloads.DTYPES[wl.dtype], wl.head_dim, wl.causal)
+    for r in (a, a + 1, a + bm - 1, a + bm, (a + b) // 2, b - bm, b - 1):
+        if a <= r < b:
+            picks.add(r)
+    for i in rng.choice(len(lengths), size=min(16, len(lengths)), replace=False):
+        s, e = int(cu[i]), int(cu[i + 1])
+        picks.update({s, e - 1, int(rng.integers(s, e))})
+    while len(picks) < count:
+        picks.add(int(rng.integers(0, wl.total_tokens)))
+    rows = sorted(picks)
+    return [(r, int(rng.integers(0, wl.heads))) for r in rows]
+
+
+@pytest.mark.parametrize("k", [4, 5])
+def test_workload_large_sampled(k):
+    wl = workloads.make_workload(k)
+    _say(f"[parity] {wl.name} B={wl.num_seqs} T={wl.total_tokens} H={wl.heads} D={wl.head_dim} "
+         f"causal={wl.causal} (sampled rows)")
+    out, lse = _gpu_forward(wl)
+    assert torch.isfinite(out.float()).all().item()
+    assert torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(77 + k)
+    samples = _sample_rows(wl, rng, 96)
+    cu = wl.cu_seqlens_host()
+    ref, ref_lse = oracle.varlen_attention_rows(wl.q, wl.k, wl.v, cu, cu, wl.scale, wl.causal, samples)
+    rows = torch.tensor([r for r, _ in samples], device=DEV)
+    heads = torch.tensor([h for _, h in samples], device=DEV)
+    got = out[rows, heads].float().cpu().numpy()
+    got_lse = lse[heads, rows].cpu().numpy()
+    err = np.max(np.abs(got - ref))
+    lerr = np.max(np.abs(got_lse - ref_lse))
+    _say(f"[parity]   {len(samples)} sampled rows: out max-abs {err:.3e} lse max-abs {lerr:.3e}")
+    assert err <= TOL_OUT[wl.dtype] and lerr <= TOL_LSE
+    # every row: causal row 0 of each sequence returns its own value row
+    first_rows = torch.from_numpy(cu[:-1]).long().to(DEV)
+    v0 = wl.v.to(DEV)[first_rows]
+    assert (out[first_rows].float() - v0.float()).abs().max().item() <= TOL_OUT[wl.dtype]
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+EDGE_DTYPES = ["fp32", "bf16", "fp16"]
+
+
+@pytest.mark.parametrize("dtype", EDGE_DTYPES)
+@pytest.mark.parametrize("head_dim", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_head_dim(dtype, head_dim, causal):
+    bm = vlp.kernel_block_m(workloads.DTYPES[dtype], head_dim, causal)
+    lengths = [1, bm - 1, bm, bm + 1, 3, 2 * bm + 5, 37]
+    wl = workloads.custom_workload(lengths, 3, head_dim, dtype, causal, seed=head_dim + 7 * causal)
+    _check_full(wl)
+
+
+@pytest.mark.parametrize("dtype", EDGE_DTYPES)
+def test_single_long_sequence(dtype):
+    wl = workloads.custom_workload([1000], 2, 64, dtype, False, seed=11)
+    _check_full(wl)
+    _check_full(wl, causal=True)
+    _check_full(wl, first_token=True)
+
+
+def test_batch_of_length_one():
+    wl = workloads.custom_workload([1] * 50, 4, 64, "bf16", False, seed=12)
+    out, lse = _check_full(wl)
+    assert torch.equal(out, wl.v.to(DEV))
+
+
+def test_zero_length_tail_and_nan_poisoned_capacity():
+    """cu_seqlens [0, .., L, L, L] over a larger physical buffer: rows >= L are
+    never written, and NaN in the unused capacity rows never leaks in."""
+    lengths = [70, 0, 33, 129, 0, 0]
+    cap_rows = 300
+    h, d = 4, 128
+    for dtype in ("bf16", "fp32"):
+        wl = workloads.custom_workload(lengths, h, d, dtype, True, seed=13)
+        t = wl.total_tokens
+        tdt = workloads.DTYPES[dtype]
+        q = torch.full((cap_rows, h, d), float("nan"), dtype=tdt)
+        k, v = q.clone(), q.clone()
+        q[:t], k[:t], v[:t] = wl.q, wl.k, wl.v
+        cu = _cu(lengths)
+        out = torch.full((cap_rows, h, d), float("nan"), dtype=tdt, device=DEV)
+        lse = torch.full((h, cap_rows), float("nan"), device=DEV)
+        vlp.varlen_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), cu.to(DEV), 0, wl.scale, True, False,
+                            out=out, lse=lse)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.varlen_attention(wl.q, wl.k, wl.v, cu.numpy(), cu.numpy(), wl.scale, True)
+        assert np.max(np.abs(out[:t].float().cpu().numpy() - ref)) <= TOL_OUT[dtype]
+        assert np.max(np.abs(lse[:, :t].cpu().numpy() - ref_lse)) <= TOL_LSE
+        assert torch.isnan(out[t:].float()).all().item() and torch.isnan(lse[:, t:]).all().item()
+
+
+def test_causal_with_longer_keys():
+    """Lq != Lk (cross-attention shapes): bottom-right causal alignment."""
+    rng = np.random.default_rng(14)
+    lq, lk = [5, 40, 1, 130], [9, 40, 7, 200]
+    h, d = 2, 64
+    for dtype in ("fp32", "bf16"):
+        tdt = workloads.DTYPES[dtype]
+        q = torch.from_numpy(rng.standard_normal((sum(lq), h, d), dtype=np.float32)).to(tdt)
+        k = torch.from_numpy(rng.standard_normal((sum(lk), h, d), dtype=np.float32)).to(tdt)
+        v = torch.from_numpy(rng.standard_normal((sum(lk), h, d), dtype=np.float32)).to(tdt)
+        cq, ck = _cu(lq), _cu(lk)
+        for causal in (False, True):
+            out, lse = vlp.varlen_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cq.to(DEV), ck.to(DEV), 0, 0.125,
+                                           causal)
+            torch.cuda.synchronize()
+            ref, ref_lse = oracle.varlen_attention(q, k, v, cq.numpy(), ck.numpy(), 0.125, causal)
+            assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= TOL_OUT[dtype]
+            assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= TOL_LSE
+
+
+def test_causal_query_sees_no_key_gives_zero_and_neg_inf():
+    """Lq > Lk with causal alignment leaves the first Lq - Lk queries keyless."""
+    h, d = 1, 64
+    q = torch.randn(6, h, d).to(torch.bfloat16)
+    k = torch.randn(2, h, d).to(torch.bfloat16)
+    v = torch.randn(2, h, d).to(torch.bfloat16)
+    cq, ck = _cu([6]), _cu([2])
+    out, lse = vlp.varlen_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cq.to(DEV), ck.to(DEV), 0, 0.125, True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.varlen_attention(q, k, v, cq.numpy(), ck.numpy(), 0.125, True)
+    assert np.all(out[:4].float().cpu().numpy() == 0) and np.all(np.isneginf(lse[:, :4].cpu().numpy()))
+    assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= 2e-2
+
+
+# --------------------------------------------------------------------------
+# invariants (bitwise on the GPU)
+# --------------------------------------------------------------------------
+
+def test_deterministic_and_schedule_independent():
+    wl = workloads.make_workload(3)
+    out1, lse1 = _gpu_forward(wl)
+    out2, lse2 = _gpu_forward(wl)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    cu = torch.from_numpy(wl.cu_seqlens_host())
+    bm = vlp.kernel_block_m(torch.bfloat16, wl.head_dim)
+    host = vlp.build_ragged_grid(cu, bm)
+    natural = vlp.RaggedGrid(host.grid_mapping.to(DEV), host.block_offsets.to(DEV), None, host.num_blocks, bm)
+    lpt = vlp.RaggedGrid(host.grid_mapping.to(DEV), host.block_offsets.to(DEV), host.tile_order.to(DEV),
+                         host.num_blocks, bm)
+    out3, lse3 = _gpu_forward(wl, grid=natural)
+    out4, lse4 = _gpu_forward(wl, grid=lpt)
+    assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
+    assert torch.equal(out1, out4) and torch.equal(lse1, lse4)
+
+
+def test_sequence_independence_bitwise():
+    wl = workloads.make_workload(3)
+    out1, lse1 = _gpu_forward(wl)
+    cu = wl.cu_seqlens_host()
+    j = 5
+    wl.k[cu[j]:cu[j + 1]] += 1.0
+    wl.v[cu[j]:cu[j + 1]] *= -1.0
+    out2, lse2 = _gpu_forward(wl)
+    keep = torch.ones(wl.total_tokens, dtype=torch.bool)
+    keep[cu[j]:cu[j + 1]] = False
+    keep = keep.to(DEV)
+    assert torch.equal(out1[keep], out2[keep]) and torch.equal(lse1[:, keep], lse2[:, keep])
+    assert not torch.equal(out1[~keep], out2[~keep])
+
+
+def test_sequence_permutation_moves_output_blocks_bitwise():
+    wl = workloads.make_workload(2)
+    out1, _ = _gpu_forward(wl)
+    cu = wl.cu_seqlens_host()
+    order = np.random.default_rng(3).permutation(wl.num_seqs)
+    idx = torch.from_numpy(np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order])).long()
+    wl2 = workloads.custom_workload(wl.lengths[order], wl.heads, wl.head_dim, wl.dtype, wl.causal, seed=0)
+    wl2.q, wl2.k, wl2.v = wl.q[idx], wl.k[idx], wl.v[idx]
+    out2, _ = _gpu_forward(wl2)
+    assert torch.equal(out2, out1[idx.to(DEV)])
+
+
+def test_host_grid_matches_device_grid_bitwise():
+    wl = workloads.make_workload(4)
+    out1, lse1 = _gpu_forward(wl)
+    cu = torch.from_numpy(wl.cu_seqlens_host())
+    bm = vlp.kernel_block_m(torch.bfloat16, wl.head_dim, True)
+    host = vlp.build_ragged_grid(cu, bm)
+    g = vlp.RaggedGrid(host.grid_mapping.to(DEV), host.block_offsets.to(DEV), host.tile_order.to(DEV),
+                       host.num_blocks, bm)
+    out2, lse2 = _gpu_forward(wl, grid=g)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)

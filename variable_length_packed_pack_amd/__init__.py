@@ -1,0 +1,212 @@
+"""Packed variable-length attention forward for AMD Instinct MI355X (gfx950).
+
+A thin Python layer over the C ABI of ``libvlp.so`` (``include/vlp.h``).  It
+only marshals arguments: torch supplies device memory and the current stream;
+every step of the computation runs in the library's C++ and HIP code.
+
+Functions mirror the pages' calls:
+
+* ``pack_sequences(lengths, max_seq_len) -> (flat_index, cu_seqlens)``
+  ("gigl.nn.packed_attention", "Data flow of a packed forward", "Example").
+* ``build_ragged_grid(cu_seqlens, block_m) -> RaggedGrid`` with grid_mapping,
+  block_offsets and the longest-first tile_order ("PyCoRa", "CoRa Metadata").
+* ``varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen, scale,
+  causal, query_is_first_token, out, lse) -> (out, lse)``
+  ("gigl.nn.packed_attention", packed_attention).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import NamedTuple, Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    VLP_BF16,
+    VLP_DEVICE_SORT_MAX_SEQS,
+    VLP_FIRST_TOKEN_BLOCK_M,
+    VLP_FP16,
+    VLP_FP32,
+    VlpError,
+)
+
+_DTYPE_CODES = {torch.float32: VLP_FP32, torch.float16: VLP_FP16, torch.bfloat16: VLP_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def load_library():
+    """Load libvlp.so (raises if it is not built)."""
+    return _lib.load()
+
+
+# ---------------------------------------------------------------------------
+# host metadata
+# ---------------------------------------------------------------------------
+
+def pack_sequences(lengths, max_seq_len: int):
+    """lengths (host, int) -> (flat_index int64 [T], cu_seqlens int32 [B+1]), CPU tensors."""
+    lib = _lib.load()
+    lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64).reshape(-1))
+    if lens.size and (lens.min() < -2**31 or lens.max() > 2**31 - 1):
+        raise _lib.VlpError(_lib.VLP_ERR_INVALID, "pack_sequences")
+    lens = lens.astype(np.int32)
+    b = int(lens.size)
+    cu = np.zeros(b + 1, dtype=np.int32)
+    total = ctypes.c_int64(0)
+    st = lib.vlp_pack_sequences(lens.ctypes.data, b, int(max_seq_len), None, 0, cu.ctypes.data,
+                                ctypes.addressof(total))
+    _lib.check(st, "pack_sequences")
+    flat = np.zeros(max(total.value, 1), dtype=np.int64)
+    st = lib.vlp_pack_sequences(lens.ctypes.data, b, int(max_seq_len), flat.ctypes.data, total.value,
+                                cu.ctypes.data, ctypes.addressof(total))
+    _lib.check(st, "pack_sequences")
+    return torch.from_numpy(flat[: total.value].copy()), torch.from_numpy(cu)
+
+
+def grid_capacity(total_tokens: int, num_seqs: int, block_m: int) -> int:
+    return int(_lib.load().vlp_grid_capacity(int(total_tokens), int(num_seqs), int(block_m)))
+
+
+class RaggedGrid(NamedTuple):
+    """Tile metadata of one batch.  On the host the arrays have exactly
+    ``num_blocks`` entries; built on the device they have ``grid_cap``
+    entries (-1 past the active tiles) and ``num_blocks`` is None because
+    it is known only on the device (block_offsets[-1])."""
+
+    grid_mapping: torch.Tensor
+    block_offsets: torch.Tensor
+    tile_order: torch.Tensor
+    num_blocks: Optional[int]
+    block_m: int
+
+
+def build_ragged_grid(cu_seqlens: torch.Tensor, block_m: int, grid_cap: Optional[int] = None) -> RaggedGrid:
+    """CoRa-style metadata for ``cu_seqlens`` with ``block_m`` rows per tile.
+
+    A CPU tensor is processed on the host; a CUDA tensor on the device (no
+    host read; ``grid_cap`` defaults to G_cap(total capacity, B, block_m)
+    which needs ``grid_cap`` or a host total, so it must be given).
+    """
+    lib = _lib.load()
+    b = int(cu_seqlens.numel()) - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens.is_cuda:
+        if grid_cap is None:
+            raise ValueError("grid_cap is required for a device build (use grid_capacity)")
+        dev = cu_seqlens.device
+        bo = torch.empty(b + 1, dtype=torch.int32, device=dev)
+        gm = torch.empty(max(grid_cap, 1), dtype=torch.int32, device=dev)
+        to = torch.empty(max(grid_cap, 1), dtype=torch.int32, device=dev)
+        st = lib.vlp_build_ragged_grid_device(_ptr(cu_seqlens.contiguous()), b, int(block_m), _ptr(bo), _ptr(gm),
+                                              _ptr(to), int(grid_cap), _stream_handle(dev))
+        _lib.check(st, "build_ragged_grid (device)")
+        return RaggedGrid(gm[:grid_cap], bo, to[:grid_cap], None, int(block_m))
+    cu = np.ascontiguousarray(cu_seqlens.numpy().astype(np.int32))
+    bo = np.zeros(b + 1, dtype=np.int32)
+    nb = ctypes.c_int64(0)
+    st = lib.vlp_build_ragged_grid(cu.ctypes.data, b, int(block_m), bo.ctypes.data, None, None, 0,
+                                   ctypes.addressof(nb))
+    _lib.check(st, "build_ragged_grid")
+    g = nb.value
+    gm = np.zeros(max(g, 1), dtype=np.int32)
+    to = np.zeros(max(g, 1), dtype=np.int32)
+    st = lib.vlp_build_ragged_grid(cu.ctypes.data, b, int(block_m), bo.ctypes.data, gm.ctypes.data,
+                                   to.ctypes.data, g, ctypes.addressof(nb))
+    _lib.check(st, "build_ragged_grid")
+    return RaggedGrid(torch.from_numpy(gm[:g].copy()), torch.from_numpy(bo), torch.from_numpy(to[:g].copy()),
+                      g, int(block_m))
+
+
+def kernel_block_m(dtype: torch.dtype, head_dim: int, causal: bool = False, query_is_first_token: bool = False,
+                   num_seqs: int = 1, rows_q: int = 0, max_seqlen: int = 0) -> int:
+    code = _DTYPE_CODES.get(dtype, -1)
+    return int(_lib.load().vlp_kernel_block_m(code, int(head_dim), int(causal), int(query_is_first_token),
+                                              int(num_seqs), int(rows_q), int(max_seqlen)))
+
+
+def workspace_size(num_seqs: int, rows_q: int, block_m: int) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().vlp_varlen_attn_workspace_size(int(num_seqs), int(rows_q), int(block_m),
+                                                          ctypes.addressof(n)), "workspace_size")
+    return int(n.value)
+
+
+# ---------------------------------------------------------------------------
+# attention forward
+# ---------------------------------------------------------------------------
+
+def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens_q: Optional[torch.Tensor], cu_seqlens_k: torch.Tensor,
+                    max_seqlen: int = 0, scale: Optional[float] = None, causal: bool = False,
+                    query_is_first_token: bool = False, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, *, return_lse: bool = True,
+                    workspace: Optional[torch.Tensor] = None, grid: Optional[RaggedGrid] = None):
+    """Packed attention forward on the current stream; returns (out, lse).
+
+    q [rows_q, H, D] (first-token mode: [num_seqs, H, D]), k/v [T_k, H, D],
+    cu_seqlens int32 [B+1] on the same device.  ``grid``: cached device
+    metadata from ``build_ragged_grid`` (host-built arrays moved to the
+    device) to skip the device grid build.
+    """
+    lib = _lib.load()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens_k.is_cuda):
+        raise ValueError("q, k, v and cu_seqlens must be device tensors")
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one of float32 / float16 / bfloat16")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q [rows, H, D] and k, v [T, H, D] with matching H, D")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    rows_q, heads, head_dim = (int(x) for x in q.shape)
+    total_k = int(k.shape[0])
+    b = int(cu_seqlens_k.numel()) - 1
+    if cu_seqlens_k.dtype != torch.int32 or (cu_seqlens_q is not None and cu_seqlens_q.dtype != torch.int32):
+        raise TypeError("cu_seqlens must be int32")
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(heads, rows_q, dtype=torch.float32, device=dev)
+    code = _DTYPE_CODES[q.dtype]
+    ft = int(bool(query_is_first_token))
+    cu_q_ptr = None if (ft and cu_seqlens_q is None) else _ptr(cu_seqlens_q)
+    stream = _stream_handle(dev)
+    if grid is not None:
+        nb = grid.num_blocks if grid.num_blocks is not None else int(grid.grid_mapping.numel())
+        st = lib.vlp_varlen_attn_fwd_grid(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b,
+                                          rows_q, total_k, heads, head_dim, int(max_seqlen), float(scale),
+                                          int(bool(causal)), ft, _ptr(out), _ptr(lse), _ptr(grid.grid_mapping),
+                                          _ptr(grid.block_offsets), _ptr(grid.tile_order), nb, grid.block_m,
+                                          stream)
+        _lib.check(st, "varlen_attn_fwd_grid")
+        return out, lse
+    if workspace is None:
+        bm = lib.vlp_kernel_block_m(code, head_dim, int(bool(causal)), ft, b, rows_q, int(max_seqlen))
+        if bm < 1:
+            raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_fwd")
+        nbytes = workspace_size(b, b if ft else rows_q, bm)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    st = lib.vlp_varlen_attn_fwd(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b, rows_q,
+                                 total_k, heads, head_dim, int(max_seqlen), float(scale), int(bool(causal)), ft,
+                                 _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()), stream)
+    _lib.check(st, "varlen_attn_fwd")
+    return out, lse

@@ -1,0 +1,206 @@
+// C ABI of libvlp.so: host-side validation, workspace layout and dispatch.
+//
+// Every argument the host can see is checked before any HIP call; device
+// buffer contents (cu_seqlens) are never read on the host, so the forward
+// path enqueues work without synchronising ("gigl.nn.packed_attention":
+// apart from the token count in pack_sequences, the packed path needs no
+// host syncs; "So you wanna CUDA Graph", "Scheduling without max_seqlen":
+// the launch is sized by G_cap, not by reading the lengths).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "tile_config.h"
+#include "vlp_internal.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+vlp_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return VLP_OK;
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", static_cast<int>(e), hipGetErrorString(e));
+  return VLP_ERR_HIP;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout of the device-built grid: [block_offsets | grid_mapping |
+// tile_order], each 256-byte aligned.
+struct GridWorkspace {
+  size_t off_bo, off_gm, off_to, bytes;
+};
+
+GridWorkspace grid_workspace(int32_t num_seqs, int64_t cap) {
+  GridWorkspace w;
+  w.off_bo = 0;
+  w.off_gm = round_up(sizeof(int32_t) * (static_cast<size_t>(num_seqs) + 1), 256);
+  w.off_to = w.off_gm + round_up(sizeof(int32_t) * static_cast<size_t>(cap), 256);
+  w.bytes = w.off_to + round_up(sizeof(int32_t) * static_cast<size_t>(cap), 256);
+  return w;
+}
+
+struct Checked {
+  int32_t block_m;
+  int64_t grid_rows;  // rows the grid is sized for
+};
+
+// Shared validation of the forward arguments; fills the tile size.
+vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void* v,
+                         const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, int64_t rows_q,
+                         int64_t total_k, int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale,
+                         int32_t causal, int32_t first_token, const void* out, Checked* c) {
+  if (!q || !k || !v || !out || !cu_k) return VLP_ERR_NULL;
+  if (!first_token && !cu_q) return VLP_ERR_NULL;
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
+  if (!vlp::head_dim_built(head_dim)) return VLP_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || heads < 1 || rows_q < 0 || total_k < 0 || max_seqlen < 0) return VLP_ERR_INVALID;
+  if ((causal != 0 && causal != 1) || (first_token != 0 && first_token != 1)) return VLP_ERR_INVALID;
+  if (!isfinite(scale)) return VLP_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VLP_ERR_INVALID;
+  if (first_token && rows_q != num_seqs) return VLP_ERR_INVALID;
+  if (rows_q > INT32_MAX || total_k > INT32_MAX) return VLP_ERR_OVERFLOW;
+  if (rows_q * static_cast<int64_t>(heads) > INT32_MAX) return VLP_ERR_OVERFLOW;
+  c->block_m = vlp_kernel_block_m(dtype, head_dim, causal, first_token, num_seqs, rows_q, max_seqlen);
+  if (c->block_m < 1) return VLP_ERR_UNSUPPORTED;
+  c->grid_rows = first_token ? num_seqs : rows_q;
+  return VLP_OK;
+}
+
+vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                        int32_t num_seqs, int64_t rows_q, int32_t heads, float scale, void* out, float* lse) {
+  vlp::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.heads = heads;
+  a.rows_q = static_cast<int32_t>(rows_q);
+  a.num_blocks = -1;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int32_t causal, int32_t first_token,
+                   int64_t slots, hipStream_t s) {
+  if (slots <= 0) return VLP_OK;
+  if (first_token) return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0, slots, s));
+  const int64_t blocks = slots * a.heads;
+  if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
+  switch (dtype) {
+    case VLP_BF16: return hip_status(vlp::launch_attn_bf16(a, head_dim, causal != 0, blocks, s));
+    case VLP_FP16: return hip_status(vlp::launch_attn_f16(a, head_dim, causal != 0, blocks, s));
+    default: return hip_status(vlp::launch_attn_f32(a, head_dim, causal != 0, blocks, s));
+  }
+}
+
+}  // namespace
+
+extern "C" int32_t vlp_kernel_block_m(int32_t dtype, int32_t head_dim, int32_t causal, int32_t first_token,
+                                      int32_t num_seqs, int64_t rows_q, int32_t max_seqlen) {
+  (void)causal;
+  (void)num_seqs;
+  (void)rows_q;
+  (void)max_seqlen;
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return -1;
+  if (!vlp::head_dim_built(head_dim)) return -1;
+  if (first_token) return VLP_FIRST_TOKEN_BLOCK_M;
+  return 32 * vlp::tile_waves(dtype, head_dim);
+}
+
+extern "C" vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int32_t block_m,
+                                                     size_t* bytes) {
+  if (!bytes) return VLP_ERR_NULL;
+  if (num_seqs < 1 || rows_q < 0 || block_m < 1) return VLP_ERR_INVALID;
+  const int64_t cap = vlp_grid_capacity(rows_q, num_seqs, block_m);
+  *bytes = grid_workspace(num_seqs, cap).bytes;
+  return VLP_OK;
+}
+
+extern "C" vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
+                                                   int32_t* block_offsets, int32_t* grid_mapping,
+                                                   int32_t* tile_order, int64_t grid_cap, void* stream) {
+  if (!cu_seqlens || !block_offsets || !grid_mapping || !tile_order) return VLP_ERR_NULL;
+  if (num_seqs < 1 || block_m < 1 || grid_cap < 0 || grid_cap > INT32_MAX) return VLP_ERR_INVALID;
+  return hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, block_m, block_offsets, grid_mapping, tile_order,
+                                           grid_cap, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                          int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                                          int32_t query_is_first_token, void* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  Checked c{};
+  vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
+                                head_dim, max_seqlen, scale, causal, query_is_first_token, out, &c);
+  if (st != VLP_OK) return st;
+  if (!workspace) return VLP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
+  const int64_t cap = vlp_grid_capacity(c.grid_rows, num_seqs, c.block_m);
+  if (cap > INT32_MAX || cap * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  const GridWorkspace w = grid_workspace(num_seqs, cap);
+  if (workspace_bytes < w.bytes) return VLP_ERR_CAPACITY;
+  if (cap == 0) return VLP_OK;
+
+  char* base = static_cast<char*>(workspace);
+  int32_t* bo = reinterpret_cast<int32_t*>(base + w.off_bo);
+  int32_t* gm = reinterpret_cast<int32_t*>(base + w.off_gm);
+  int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* grid_cu = query_is_first_token ? cu_seqlens_k : cu_seqlens_q;
+  st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, s));
+  if (st != VLP_OK) return st;
+
+  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse);
+  a.grid_mapping = gm;
+  a.block_offsets = bo;
+  a.tile_order = to;
+  a.grid_cap = static_cast<int32_t>(cap);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, s);
+}
+
+extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k, const void* v,
+                                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                               int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                               int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                                               int32_t query_is_first_token, void* out, float* lse,
+                                               const int32_t* grid_mapping, const int32_t* block_offsets,
+                                               const int32_t* tile_order, int64_t num_blocks, int32_t block_m,
+                                               void* stream) {
+  Checked c{};
+  vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
+                                head_dim, max_seqlen, scale, causal, query_is_first_token, out, &c);
+  if (st != VLP_OK) return st;
+  if (!grid_mapping || !block_offsets) return VLP_ERR_NULL;
+  if (num_blocks < 0 || block_m != c.block_m) return VLP_ERR_INVALID;
+  if (num_blocks > INT32_MAX || num_blocks * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse);
+  a.grid_mapping = grid_mapping;
+  a.block_offsets = block_offsets;
+  a.tile_order = tile_order;
+  a.num_blocks = static_cast<int32_t>(num_blocks);
+  a.grid_cap = static_cast<int32_t>(num_blocks);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks,
+                 static_cast<hipStream_t>(stream));
+}
+
+extern "C" const char* vlp_status_string(vlp_status status) {
+  switch (status) {
+    case VLP_OK: return "VLP_OK";
+    case VLP_ERR_NULL: return "VLP_ERR_NULL: a required pointer is NULL";
+    case VLP_ERR_INVALID: return "VLP_ERR_INVALID: an argument is out of contract";
+    case VLP_ERR_UNSUPPORTED: return "VLP_ERR_UNSUPPORTED: dtype, head_dim or mode not built";
+    case VLP_ERR_CAPACITY: return "VLP_ERR_CAPACITY: an output or workspace buffer is too small";
+    case VLP_ERR_OVERFLOW: return "VLP_ERR_OVERFLOW: a count does not fit in int32";
+    case VLP_ERR_HIP: return g_hip_error;
+    default: return "unknown vlp status";
+  }
+}

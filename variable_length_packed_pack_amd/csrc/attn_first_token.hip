@@ -1,0 +1,243 @@
+// First-token packed attention: one query per sequence.
+//
+// "gigl.nn.packed_attention", packed_attention with query_is_first_token:
+// only each sequence's first token is queried (the anchor readout of the
+// last layer); query row i belongs to sequence i and sees all of that
+// sequence's keys (causal: only key 0, the query sits at position 0).
+//
+// The work is 4*Lk*D flops against 2*Lk*D*elt bytes of K/V per (sequence,
+// head): bandwidth-bound, so no matrix cores.  One wavefront per (sequence,
+// head), four heads per workgroup.  A key row of one head is split into
+// 16-byte chunks over LPK lanes; the wave covers KPS = 64/LPK keys per step
+// and U steps per round (U*KPS keys in flight) for memory parallelism.  Each
+// key slot keeps its own online-softmax state; slots merge at the end.
+// Sequences run in tile_order (longest first) through the same ragged-grid
+// metadata as the tiled kernel, with one tile per sequence.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vlp_internal.h"
+
+namespace vlp {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Chunk;  // 16 bytes of one key row, widened to fp32
+
+template <> struct Chunk<VLP_FP32> {
+  static constexpr int N = 4;
+  // Whole-vector bit casts only: this compiler reads element 0 when
+  // __builtin_bit_cast is applied directly to a vector subscript.
+  static __device__ __forceinline__ void widen(u32x4_t r, float (&x)[N]) {
+    const f32x4_t f = __builtin_bit_cast(f32x4_t, r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = f[i];
+  }
+  static __device__ __forceinline__ u32x4_t narrow(const float (&x)[N]) {
+    f32x4_t f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = x[i];
+    return __builtin_bit_cast(u32x4_t, f);
+  }
+};
+
+template <> struct Chunk<VLP_BF16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void widen(u32x4_t r, float (&x)[N]) {
+    const f32x4_t lo = __builtin_bit_cast(f32x4_t, r << 16);           // even elements
+    const f32x4_t hi = __builtin_bit_cast(f32x4_t, r & 0xffff0000u);   // odd elements
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = lo[i];
+      x[2 * i + 1] = hi[i];
+    }
+  }
+  static __device__ __forceinline__ u32x4_t narrow(const float (&x)[N]) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x2_t p;
+      p[0] = static_cast<__bf16>(x[2 * i]);
+      p[1] = static_cast<__bf16>(x[2 * i + 1]);
+      r[i] = __builtin_bit_cast(uint32_t, p);
+    }
+    return r;
+  }
+};
+
+template <> struct Chunk<VLP_FP16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void widen(u32x4_t r, float (&x)[N]) {
+    const f16x8_t h = __builtin_bit_cast(f16x8_t, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(h[i]);
+  }
+  static __device__ __forceinline__ u32x4_t narrow(const float (&x)[N]) {
+    f16x8_t h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[i]);
+    return __builtin_bit_cast(u32x4_t, h);
+  }
+};
+
+// Merge two online-softmax states (m in log2 units).
+template <int N>
+__device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N], float mo, float lo,
+                                            const float (&acco)[N]) {
+  const float mn = fmaxf(m, mo);
+  if (mn == kNegInf) return;  // both empty
+  const float sa = __builtin_amdgcn_exp2f(m - mn);
+  const float sb = __builtin_amdgcn_exp2f(mo - mn);
+  l = l * sa + lo * sb;
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = acc[e] * sa + acco[e] * sb;
+  m = mn;
+}
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a, int head_groups) {
+  using C = Chunk<DT>;
+  constexpr int EPC = C::N;        // elements per 16-byte chunk
+  constexpr int LPK = D / EPC;     // lanes per key row
+  constexpr int KPS = 64 / LPK;    // keys per step
+  constexpr int U = 4;             // steps per round
+  static_assert(LPK >= 1 && LPK <= 64 && (LPK & (LPK - 1)) == 0, "lanes per key");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = static_cast<int>(blockIdx.x) / head_groups;
+  const int head = (static_cast<int>(blockIdx.x) - slot * head_groups) * 4 + wave;
+  const int g_active = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
+  if (slot >= g_active || slot >= a.grid_cap || head >= a.heads) return;  // no barriers below
+  const int f = a.tile_order ? a.tile_order[slot] : slot;
+  if (f < 0 || f >= a.grid_cap) return;
+  const int seq = a.grid_mapping[f];
+  if (seq < 0 || seq >= a.num_seqs) return;
+  const int k_start = a.cu_k[seq];
+  const int lk = a.cu_k[seq + 1] - k_start;
+  const int lk_vis = CAUSAL ? min(lk, 1) : lk;
+
+  const int grp = lane / LPK;   // key slot within a step
+  const int c = lane % LPK;     // chunk of the row
+  const size_t rs = static_cast<size_t>(a.heads) * D;
+
+  float qf[EPC];
+  {
+    const char* qp = static_cast<const char*>(a.q) +
+                     ((static_cast<size_t>(seq) * a.heads + head) * D + c * EPC) * (16 / EPC);
+    C::widen(*reinterpret_cast<const u32x4_t*>(qp), qf);
+  }
+  const char* kp = static_cast<const char*>(a.k) +
+                   ((static_cast<size_t>(k_start) * a.heads + head) * D + c * EPC) * (16 / EPC);
+  const char* vp = static_cast<const char*>(a.v) +
+                   ((static_cast<size_t>(k_start) * a.heads + head) * D + c * EPC) * (16 / EPC);
+  const size_t row_bytes = rs * (16 / EPC);
+
+  float m = kNegInf, l = 0.0f, acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+
+  for (int j0 = 0; j0 < lk_vis; j0 += U * KPS) {
+    u32x4_t kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * KPS + grp;
+      kr[u] = u32x4_t{0, 0, 0, 0};
+      vr[u] = kr[u];
+      if (j < lk_vis) {
+        kr[u] = *reinterpret_cast<const u32x4_t*>(kp + j * row_bytes);
+        vr[u] = *reinterpret_cast<const u32x4_t*>(vp + j * row_bytes);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * KPS + grp;
+      float kf[EPC];
+      C::widen(kr[u], kf);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1) dot += __shfl_xor(dot, off);
+      if (j < lk_vis) {
+        const float s = dot * a.scale_log2;
+        const float mn = fmaxf(m, s);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        const float p = __builtin_amdgcn_exp2f(s - mn);
+        float vf[EPC];
+        C::widen(vr[u], vf);
+        l = l * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = __builtin_fmaf(p, vf[e], acc[e] * alpha);
+        m = mn;
+      }
+    }
+  }
+
+  // Merge the KPS key slots (lanes that differ in the grp bits).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    float acco[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acco[e] = __shfl_xor(acc[e], off);
+    merge_state<EPC>(m, l, acc, mo, lo, acco);
+  }
+
+  if (grp == 0) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float o[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) o[e] = acc[e] * inv;
+    char* op = static_cast<char*>(a.out) +
+               ((static_cast<size_t>(seq) * a.heads + head) * D + c * EPC) * (16 / EPC);
+    *reinterpret_cast<u32x4_t*>(op) = C::narrow(o);
+    if (c == 0 && a.lse)
+      a.lse[static_cast<size_t>(head) * a.rows_q + seq] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_dt_d(const AttnArgs& a, bool causal, int64_t slots, hipStream_t s) {
+  const int head_groups = (a.heads + 3) / 4;
+  const dim3 grid(static_cast<unsigned>(slots * head_groups));
+  if (causal)
+    hipLaunchKernelGGL((attn_first_token_kernel<DT, D, true>), grid, dim3(256), 0, s, a, head_groups);
+  else
+    hipLaunchKernelGGL((attn_first_token_kernel<DT, D, false>), grid, dim3(256), 0, s, a, head_groups);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, int64_t slots, hipStream_t s) {
+  switch (head_dim) {
+    case 16: return launch_dt_d<DT, 16>(a, causal, slots, s);
+    case 32: return launch_dt_d<DT, 32>(a, causal, slots, s);
+    case 64: return launch_dt_d<DT, 64>(a, causal, slots, s);
+    case 128: return launch_dt_d<DT, 128>(a, causal, slots, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
+                                   int64_t slots, hipStream_t s) {
+  if (slots <= 0) return hipSuccess;
+  switch (dtype) {
+    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, slots, s);
+    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, slots, s);
+    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, slots, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vlp

@@ -1,0 +1,62 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP
+// translation units.  Not installed; the public surface is include/vlp.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vlp.h"
+
+namespace vlp {
+
+// Arguments of one attention launch, passed by value to the kernels.
+// Tile metadata follows "PyCoRa", "CoRa Metadata": flat tile f belongs to
+// sequence grid_mapping[f] and is its local tile f - block_offsets[seq];
+// workgroup slot s runs flat tile tile_order[s] (or s when tile_order is NULL).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;                  // [heads, rows_q] or nullptr
+  const int32_t* cu_q;         // [num_seqs + 1] (unused in first-token mode)
+  const int32_t* cu_k;         // [num_seqs + 1]
+  const int32_t* grid_mapping; // [>= G]
+  const int32_t* block_offsets;// [num_seqs + 1]
+  const int32_t* tile_order;   // [>= G] or nullptr
+  int32_t num_seqs;
+  int32_t heads;
+  int32_t rows_q;
+  int32_t num_blocks;          // G when known on the host, -1: read block_offsets[num_seqs]
+  int32_t grid_cap;            // entries of grid_mapping / tile_order (guards bad metadata)
+  float scale_log2;            // scale * log2(e): scores go straight to exp2
+};
+
+// Kernel families and their tile shapes.  block_m is the query rows per
+// workgroup tile; it is what the ragged grid is built with.
+struct TileShape {
+  int block_m;   // query rows per workgroup
+  int block_n;   // keys per inner step
+  int waves;     // wavefronts per workgroup
+};
+
+// Tile shape vlp_varlen_attn_fwd uses for (dtype, head_dim); block_m = 0 if
+// the pair is not built.
+TileShape attn_tile_shape(int dtype, int head_dim);
+
+// Launch the tiled MFMA forward for `blocks` workgroups (slots * heads).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+
+// First-token forward: one wavefront per (sequence, head), `slots` sequences.
+hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
+                                   int64_t slots, hipStream_t s);
+
+// Device ragged-grid build (one workgroup).
+hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
+                             int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
+                             int64_t grid_cap, hipStream_t s);
+
+}  // namespace vlp
