@@ -34,9 +34,11 @@
 // with the same S^T / O^T orientation; there V needs no transpose because
 // each A operand is a single element.
 //
-// Masking: keys past the sequence end are zero-filled in LDS (never read
-// from the next sequence's rows, so NaN * 0 cannot leak in -- "So you wanna
-// CUDA Graph", "Correctness tangent") and their scores set to -inf; causal
+// Masking: key rows past the sequence end are never read from memory (the
+// 16-bit path re-reads the sequence's last row in their place, the fp32 path
+// zero-fills), so nothing outside the sequence -- such as NaN in unused
+// capacity rows, "So you wanna CUDA Graph", "Correctness tangent" -- can
+// reach the result; their scores are set to -inf (probability 0); causal
 // masking is bottom-right aligned in local positions (key j visible to query
 // p iff j <= p + Lk - Lq).  Partial edge tiles are masked, never padded.
 #pragma once
@@ -122,33 +124,51 @@ __device__ __forceinline__ bool decode_workgroup(const AttnArgs& a, TileCoord& t
   return true;
 }
 
-// Online-softmax update for one block of scores held as NS registers of
-// 16 values per lane.  Returns the per-row factor that rescales the running
-// output; updates m (running max, log2 units) and l (this half-wave's sum),
-// and overwrites s with the unnormalised probabilities.
-template <int NS>
-__device__ __forceinline__ float online_softmax(f32x16_t (&s)[NS], float& m, float& l, float scale_log2) {
-  float mx = kNegInf;
+// Online-softmax step for one block of scores held as NS registers of 16
+// values per lane (scores of one query row per lane; see the header comment).
+// The reference max m (log2 units) moves lazily: only when some row of the
+// wave meets a block max more than kRescaleLog2 above it are the running
+// output and sum rescaled, for the whole wave at once.  Between rescales the
+// probabilities exp2(s*c - m) may reach 2^kRescaleLog2, which the fp32 sum
+// and the bf16/fp16/fp32 P operand hold without loss of range; the final
+// normalisation uses the same m, so the result is the exact softmax.
+// Overwrites s with the unnormalised probabilities; l is this half-wave's
+// partial row sum.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int NS, int NA>
+__device__ __forceinline__ void softmax_step(f32x16_t (&s)[NS], f32x16_t (&acc)[NA], float& m, float& l,
+                                             float scale_log2) {
+  // Four independent max / sum chains instead of one long dependent chain.
+  float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
   for (int i = 0; i < NS; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
+    for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[i][r]);
+  float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx * scale_log2);
-  const float m_use = m_new == kNegInf ? 0.0f : m_new;
-  const float alpha = fast_exp2(m - m_use);
-  float sum = 0.0f;
+  const float mt = mx * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleLog2)) {
+    const float m_new = fmaxf(m, mt);
+    const float alpha = m_new == kNegInf ? 1.0f : fast_exp2(m - m_new);
+#pragma unroll
+    for (int d = 0; d < NA; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    l *= alpha;
+    m = m_new;
+  }
+  const float m_use = m == kNegInf ? 0.0f : m;
+  float sum4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < NS; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = fast_exp2(__builtin_fmaf(s[i][r], scale_log2, -m_use));
       s[i][r] = p;
-      sum += p;
+      sum4[r & 3] += p;
     }
-  l = l * alpha + sum;
-  m = m_new;
-  return alpha;
+  l += (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
 }
 
 // Sets scores of invisible keys to -inf.  kb: first key of the block;
@@ -168,30 +188,41 @@ __device__ __forceinline__ void mask_scores(f32x16_t (&s)[NS], int kb, int hh, i
 
 // ---------------------------------------------------------------------------
 // 16-bit inputs (bf16 / fp16)
+//
+// Pipeline per key block (BN keys): the block's K (row-major) and V
+// (transposed) sit in one of two LDS buffers; while the waves run QK^T,
+// softmax and PV on it, the next block is already in the other buffer and
+// the one after is in flight from HBM into registers.  One workgroup barrier
+// per block.  Waves whose rows see none of a block's keys (causal) skip its
+// arithmetic but still share the loads and the barrier.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_h16(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   static_assert(D % 32 == 0 || D == 16, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   using E = Half16<DT>;
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
-  constexpr int KS = (D < 16 ? 1 : D / 16);     // k-steps of QK^T
+  constexpr int KS = D / 16;                    // k-steps of QK^T
   constexpr int DT32 = (D + 31) / 32;           // 32-wide output column tiles
-  constexpr int NS = BN / 32;                   // 32-key score tiles per step
+  constexpr int NS = BN / 32;                   // 32-key score tiles per block
   constexpr int KSTR = D + 8;                   // K tile row stride (elements)
   constexpr int VSTR = BN + 8;                  // transposed V row stride
   constexpr int DCH = D / 8;                    // 16-byte chunks per row
+  constexpr int KTASKS = BN * DCH;              // 16-byte K chunks per block
+  constexpr int KIT = (KTASKS + NT - 1) / NT;
+  constexpr int VTASKS = (BN / 4) * DCH;        // (4 keys x 8 columns) V tasks per block
+  constexpr int VIT = (VTASKS + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[(DT32 * 32) * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][(DT32 * 32) * VSTR];
 
   TileCoord tc;
   if (!decode_workgroup(a, tc)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int row0 = tc.tile * BM;
@@ -211,18 +242,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_h16(const AttnArgs a) {
   if (CAUSAL) wave_kv_end = min(tc.lk, min(wrow0 + 32, tc.lq) + diag);
 
   // Q^T operand: this lane's query row, k-chunk hh of every 16-wide step.
+  // Rows past the sequence end load the last real row instead (their
+  // results are never stored), so every load is unconditional.
   u32x4_t qv[KS];
   {
+    const int qrow = min(my_row, tc.lq - 1);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(tc.q_start + my_row) * a.heads + tc.head) * D;
+                         (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      if (D >= 16 && row_ok)
-        qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
-      else
-        qv[k] = u32x4_t{0, 0, 0, 0};
-    }
+    for (int k = 0; k < KS; ++k) qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
   }
+  // Keep the Q loads ahead of the K/V prologue: if they were issued after it,
+  // the wait for Q inside the loop would also wait out every K/V prefetch.
+  __builtin_amdgcn_sched_barrier(0);
 
   f32x16_t acc[DT32];
 #pragma unroll
@@ -237,77 +269,116 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_h16(const AttnArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) +
                           (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * D;
 
-  for (int it = 0; it < nblocks; ++it) {
-    const int kb = it * BN;
-    __syncthreads();
-    // K tile, row-major, 16-byte chunks (consecutive threads: consecutive chunks of a row).
-    for (int c = tid; c < BN * DCH; c += NT) {
-      const int r = c / DCH, col = c - (c / DCH) * DCH;
-      u32x4_t val = u32x4_t{0, 0, 0, 0};
-      if (kb + r < tc.lk) val = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)(kb + r) * rs + col * 8);
-      *reinterpret_cast<u32x4_t*>(&ks_lds[r * KSTR + col * 8]) = val;
-    }
-    // V tile, transposed: four consecutive keys x 8 columns per thread.
-    for (int c = tid; c < (BN / 4) * DCH; c += NT) {
-      const int quad = c / DCH, col = c - (c / DCH) * DCH;
-      u32x4_t rv[4];
+  // Register staging of one key block in 16-byte chunks.  Rows past the
+  // sequence end load the sequence's last row instead: their scores are
+  // masked to -inf (probability 0), so no value from outside the sequence is
+  // ever read and every load is unconditional (no per-lane branches, which
+  // keeps the compiler's load counting exact and the prefetch in flight).
+  u32x4_t kpre[KIT];
+  u32x4_t vpre[VIT][4];
+  const int last_row = tc.lk - 1;
+  auto load_block = [&](int kb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = kb + 4 * quad + j;
-        rv[j] = u32x4_t{0, 0, 0, 0};
-        if (key < tc.lk) rv[j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * rs + col * 8);
-      }
-      const int slot = vslot(4 * quad);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t k0 = (rv[0][w] >> sh) & 0xffffu, k1 = (rv[1][w] >> sh) & 0xffffu;
-        const uint32_t k2 = (rv[2][w] >> sh) & 0xffffu, k3 = (rv[3][w] >> sh) & 0xffffu;
-        u32x2_t pk;
-        pk[0] = k0 | (k1 << 16);
-        pk[1] = k2 | (k3 << 16);
-        *reinterpret_cast<u32x2_t*>(&vt_lds[(col * 8 + e) * VSTR + slot]) = pk;
+    for (int i = 0; i < KIT; ++i) {
+      const int c = tid + i * NT;
+      if (KTASKS % NT == 0 || c < KTASKS) {
+        const int r = min(kb + c / DCH, last_row), col = c % DCH;
+        kpre[i] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)r * rs + col * 8);
       }
     }
-    __syncthreads();
-    if (!wave_live || kb >= wave_kv_end) continue;
-
-    // S^T = K Q^T for NS tiles of 32 keys.
-    f32x16_t s[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = 0; i < VIT; ++i) {
+      const int c = tid + i * NT;
+      if (VTASKS % NT == 0 || c < VTASKS) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const u32x4_t kop = *reinterpret_cast<const u32x4_t*>(&ks_lds[(32 * i + n) * KSTR + 16 * k + 8 * hh]);
-        s[i] = E::mfma(kop, qv[k], s[i]);
-      }
-    }
-    const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
-    if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
-    const float alpha = online_softmax<NS>(s, m, l, a.scale_log2);
-#pragma unroll
-    for (int d = 0; d < DT32; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4_t pop;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pop[j] = E::pack2(s[i][8 * kk + 2 * j], s[i][8 * kk + 2 * j + 1]);
-#pragma unroll
-        for (int d = 0; d < DT32; ++d) {
-          const u32x4_t vop =
-              *reinterpret_cast<const u32x4_t*>(&vt_lds[(32 * d + n) * VSTR + 32 * i + 16 * kk + 8 * hh]);
-          acc[d] = E::mfma(vop, pop, acc[d]);
+        for (int j = 0; j < 4; ++j) {
+          const int key = min(kb + 4 * (c / DCH) + j, last_row);
+          vpre[i][j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * rs + (c % DCH) * 8);
         }
       }
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KIT; ++i) {
+      const int c = tid + i * NT;
+      if (KTASKS % NT == 0 || c < KTASKS) {
+        const int r = c / DCH, col = c % DCH;
+        *reinterpret_cast<u32x4_t*>(&ks_lds[buf][r * KSTR + col * 8]) = kpre[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+      const int c = tid + i * NT;
+      if (VTASKS % NT == 0 || c < VTASKS) {
+        const int quad = c / DCH, col = c % DCH;
+        const int slot = vslot(4 * quad);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const int sh = (e & 1) * 16;
+          u32x2_t pk;
+          pk[0] = ((vpre[i][0][w] >> sh) & 0xffffu) | (((vpre[i][1][w] >> sh) & 0xffffu) << 16);
+          pk[1] = ((vpre[i][2][w] >> sh) & 0xffffu) | (((vpre[i][3][w] >> sh) & 0xffffu) << 16);
+          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(col * 8 + e) * VSTR + slot]) = pk;
+        }
+      }
+    }
+  };
+
+  // The loop sits inside this branch so that no path reaches it with the Q
+  // loads still in flight (which would make every iteration wait for all
+  // outstanding loads, prefetch included).  nblocks is uniform over the
+  // workgroup, so the barriers inside are too.
+  if (nblocks > 0) {
+    load_block(0);
+    store_block(0);
+    if (nblocks > 1) load_block(BN);
+    __syncthreads();
+
+  for (int it = 0; it < nblocks; ++it) {
+    const int buf = it & 1;
+    const int kb = it * BN;
+    if (wave_live && kb < wave_kv_end) {
+      // S^T = K Q^T for NS tiles of 32 keys.
+      f32x16_t s[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const u32x4_t kop =
+              *reinterpret_cast<const u32x4_t*>(&ks_lds[buf][(32 * i + n) * KSTR + 16 * k + 8 * hh]);
+          s[i] = E::mfma(kop, qv[k], s[i]);
+        }
+      }
+      const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
+      if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
+      softmax_step<NS, DT32>(s, acc, m, l, a.scale_log2);
+
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4_t pop;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pop[j] = E::pack2(s[i][8 * kk + 2 * j], s[i][8 * kk + 2 * j + 1]);
+#pragma unroll
+          for (int d = 0; d < DT32; ++d) {
+            const u32x4_t vop = *reinterpret_cast<const u32x4_t*>(
+                &vt_lds[buf][(32 * d + n) * VSTR + 32 * i + 16 * kk + 8 * hh]);
+            acc[d] = E::mfma(vop, pop, acc[d]);
+          }
+        }
+    }
+    if (it + 1 < nblocks) {
+      store_block(buf ^ 1);                         // block it+1, loaded one block ago
+      if (it + 2 < nblocks) load_block((it + 2) * BN);
+    }
+    __syncthreads();
+  }
   }
 
   // Epilogue: normalise, round to the element type, store real rows only.
@@ -427,11 +498,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
     }
     const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
     if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
-    const float alpha = online_softmax<NS>(s, m, l, a.scale_log2);
-#pragma unroll
-    for (int d = 0; d < DT32; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    softmax_step<NS, DT32>(s, acc, m, l, a.scale_log2);
 
     // O^T += V^T P^T, one key pair per MFMA: half hh supplies the key its
     // score register r holds.
