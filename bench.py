@@ -189,6 +189,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
+                         "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -204,8 +207,17 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    vlp.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": nbytes, "launches": 3}), flush=True)
+        return 0
+    vlp.load_library()
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)

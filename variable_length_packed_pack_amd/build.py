@@ -69,7 +69,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             if err.strip():
                 print(f"--- {src}\n{err}", file=sys.stderr)
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol (such as a kernel stub the host pass did
+    # not emit) fails the link instead of the first dlopen.
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -25,20 +25,20 @@
 // (each half keeps a partial sum until the end).  The output is formed
 // transposed too, O^T = V^T P^T, with P^T taken straight from the score
 // registers as the B operand: the 8 P values a lane passes for k-step kk are
-// keys 16*kk + 8*(j/4) + 4*hh + (j%4), j < 8, so V is stored transposed in LDS
-// with the key order inside every 16-key group permuted to match (bits 2 and
-// 3 of the key offset swapped); then each A operand is one 16-byte LDS read.
-// Every per-query quantity (running max, sum, rescale factor) is lane-local.
+// keys 16*kk + 8*(j/4) + 4*hh + (j%4), j < 8.  For 16-bit inputs the matching
+// V^T operand comes from a row-major V tile through gfx950's transposing LDS
+// read (see the 16-bit section).  Every per-query quantity (running max, sum,
+// rescale factor) is lane-local.
 //
 // fp32 inputs use v_mfma_f32_32x32x2_f32 (A/B: one element per lane, k = hh)
 // with the same S^T / O^T orientation; there V needs no transpose because
 // each A operand is a single element.
 //
 // Masking: key rows past the sequence end are never read from memory (the
-// 16-bit path re-reads the sequence's last row in their place, the fp32 path
-// zero-fills), so nothing outside the sequence -- such as NaN in unused
-// capacity rows, "So you wanna CUDA Graph", "Correctness tangent" -- can
-// reach the result; their scores are set to -inf (probability 0); causal
+// 16-bit path's buffer loads return zeros past the sequence's last row, the
+// fp32 path zero-fills), so nothing outside the sequence -- such as NaN in
+// unused capacity rows, "So you wanna CUDA Graph", "Correctness tangent" --
+// can reach the result; their scores are set to -inf (probability 0); causal
 // masking is bottom-right aligned in local positions (key j visible to query
 // p iff j <= p + Lk - Lq).  Partial edge tiles are masked, never padded.
 #pragma once
@@ -93,12 +93,6 @@ template <> struct Half16<VLP_FP16> {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Swap bits 2 and 3 of a key offset: the slot a key occupies in the
-// transposed V tile (see the header comment).
-__device__ __forceinline__ int vslot(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 // Workgroup -> (sequence, local tile) through the ragged-grid metadata.
 struct TileCoord {
@@ -189,33 +183,74 @@ __device__ __forceinline__ void mask_scores(f32x16_t (&s)[NS], int kb, int hh, i
 // ---------------------------------------------------------------------------
 // 16-bit inputs (bf16 / fp16)
 //
-// Pipeline per key block (BN keys): the block's K (row-major) and V
-// (transposed) sit in one of two LDS buffers; while the waves run QK^T,
-// softmax and PV on it, the next block is already in the other buffer and
-// the one after is in flight from HBM into registers.  One workgroup barrier
-// per block.  Waves whose rows see none of a block's keys (causal) skip its
-// arithmetic but still share the loads and the barrier.
+// LDS tiles.  K and V of one key block are both kept row-major (key rows of
+// D elements) in LDS, 16-byte chunks XOR-swizzled per row (chunk_swz) so
+// that both operand reads below are free of bank conflicts:
+//   * K as the A operand of S^T = K Q^T: lane (n, hh) reads row 32i+n, chunk
+//     2k+hh with one ds_read_b128.
+//   * V^T as the A operand of O^T = V^T P^T: gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16) gathers, within each group of 16 lanes, four key
+//     rows x 16 columns and hands every lane four consecutive keys of one
+//     column.  Two such reads give the eight keys 16kk + 4hh + {0..3, 8..11}
+//     that this lane's P^T operand holds for k-step kk, so neither V nor P
+//     is permuted anywhere.
+// Tiles are filled by direct buffer-to-LDS loads (each lane moves one
+// 16-byte chunk; 64 lanes fill 1 KB of LDS per instruction), so the block in
+// flight occupies no registers.  The buffer descriptor of a key block ends at
+// the sequence's last row, and the hardware returns zeros past it: no value
+// outside the sequence -- NaN in unused capacity rows, "So you wanna CUDA
+// Graph", "Correctness tangent" -- is ever read, and those keys' scores are
+// masked to -inf.
+//
+// Pipeline: two LDS buffers; while the waves compute on block j, block j+1
+// streams into the other buffer; one workgroup barrier per block.  The loop
+// is unrolled by two so that every LDS access names its buffer statically.
 // ---------------------------------------------------------------------------
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define VLP_LDS __attribute__((address_space(3)))
+
+// Chunk swizzle of a tile row (chunks of 16 bytes, D/8 per row).
+//   D = 128: a row is 256 bytes, all 64 banks.  Rows r..r+15 (K reads) must
+//            take 16 different chunk slots, and rows 4m..4m+3 (transposed V
+//            reads, 2 adjacent chunks each) must too.
+//   D = 64:  two rows share the 64 banks; the even (odd) rows among 16
+//            consecutive ones need distinct slots, and rows 4m, 4m+2 (and
+//            4m+1, 4m+3) must land in different groups of four slots.
+//   D <= 32: not swizzled (edge-case sizes).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else if constexpr (D == 64) {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+  } else {
+    return 0;
+  }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (to 0).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DT, int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
-  static_assert(D % 32 == 0 || D == 16, "head_dim");
+  static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   using E = Half16<DT>;
   constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int KS = D / 16;                    // k-steps of QK^T
-  constexpr int DT32 = (D + 31) / 32;           // 32-wide output column tiles
-  constexpr int NS = BN / 32;                   // 32-key score tiles per block
-  constexpr int KSTR = D + 8;                   // K tile row stride (elements)
-  constexpr int VSTR = BN + 8;                  // transposed V row stride
-  constexpr int DCH = D / 8;                    // 16-byte chunks per row
-  constexpr int KTASKS = BN * DCH;              // 16-byte K chunks per block
-  constexpr int KIT = (KTASKS + NT - 1) / NT;
-  constexpr int VTASKS = (BN / 4) * DCH;        // (4 keys x 8 columns) V tasks per block
-  constexpr int VIT = (VTASKS + NT - 1) / NT;
+  constexpr int KS = D / 16;           // k-steps of QK^T
+  constexpr int DT32 = (D + 31) / 32;  // 32-wide output column tiles
+  constexpr int NS = BN / 32;          // 32-key score tiles per block
+  constexpr int RB = D * 2;            // bytes per tile row
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;        // rows filled by one 1 KB direct load
+  constexpr int LPT = BN / RPI;        // direct loads per tile
+  static_assert(LPT % NW == 0, "tile loads must split evenly over the waves");
+  constexpr int LPW = LPT / NW;        // direct loads per tile per wave
+  constexpr int TILE = BN * RB;        // bytes of one K (or V) tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][(DT32 * 32) * VSTR];
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
 
   TileCoord tc;
   if (!decode_workgroup(a, tc)) return;
@@ -231,7 +266,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const size_t rs = static_cast<size_t>(a.heads) * D;  // token row stride
+  const int rs_bytes = a.heads * D * 2;  // bytes between consecutive tokens of one head
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -252,9 +287,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
   }
-  // Keep the Q loads ahead of the K/V prologue: if they were issued after it,
-  // the wait for Q inside the loop would also wait out every K/V prefetch.
-  __builtin_amdgcn_sched_barrier(0);
+
+  // Direct-load lane offsets (bytes, relative to the key block's first row):
+  // load j of a tile fills rows j*RPI .. j*RPI+RPI-1; lane -> (row, slot),
+  // and the slot holds logical chunk slot ^ chunk_swz(row).  K and V share
+  // them.
+  int voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = wave * LPW + i;
+    const int r = j * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ chunk_swz<D>(r);
+    voff[i] = r * rs_bytes + c * 16;
+  }
+  // K operand: row 32i+n, logical chunk 2k+hh (the row's swizzle depends on
+  // n only, since 32 | 32i).
+  int koff[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) koff[k] = n * RB + (((2 * k + hh) ^ chunk_swz<D>(n)) << 4);
+  // V^T operand by transposing reads: lane = 16g + s; group g covers key
+  // rows base + 0..3 (base = 32i + 16kk + 8e + 4(g>>1)) and columns
+  // 32dt + 16(g&1) + 0..15; lane s points at row base + (s>>2), columns
+  // +4(s&3) .. +4(s&3)+3.
+  int vtoff[2][DT32];
+  {
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 8 * e + 4 * (g >> 1) + (s >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt) {
+        const int dcol = (32 * dt + 16 * (g & 1) + 4 * (s & 3)) & (D - 1);
+        vtoff[e][dt] = r * RB + ((((dcol >> 3) ^ chunk_swz<D>(r)) << 4) | ((dcol & 7) * 2));
+      }
+    }
+  }
 
   f32x16_t acc[DT32];
 #pragma unroll
@@ -264,121 +331,86 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   float m = kNegInf;
   float l = 0.0f;
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) +
-                          (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) +
-                          (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * D;
+  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
+  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
 
-  // Register staging of one key block in 16-byte chunks.  Rows past the
-  // sequence end load the sequence's last row instead: their scores are
-  // masked to -inf (probability 0), so no value from outside the sequence is
-  // ever read and every load is unconditional (no per-lane branches, which
-  // keeps the compiler's load counting exact and the prefetch in flight).
-  u32x4_t kpre[KIT];
-  u32x4_t vpre[VIT][4];
-  const int last_row = tc.lk - 1;
-  auto load_block = [&](int kb) {
+  // Stream key block [kb, kb + BN) of K and V into one LDS buffer.
+  auto issue_block = [&](int kb, char* buf) {
+    const int nrows = min(BN, tc.lk - kb);
+    const int nrec = (nrows - 1) * rs_bytes + RB;
+    const size_t boff = static_cast<size_t>(kb) * rs_bytes;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kseq + boff), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vseq + boff), 0, nrec, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int c = tid + i * NT;
-      if (KTASKS % NT == 0 || c < KTASKS) {
-        const int r = min(kb + c / DCH, last_row), col = c % DCH;
-        kpre[i] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)r * rs + col * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int c = tid + i * NT;
-      if (VTASKS % NT == 0 || c < VTASKS) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = min(kb + 4 * (c / DCH) + j, last_row);
-          vpre[i][j] = *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * rs + (c % DCH) * 8);
-        }
-      }
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int c = tid + i * NT;
-      if (KTASKS % NT == 0 || c < KTASKS) {
-        const int r = c / DCH, col = c % DCH;
-        *reinterpret_cast<u32x4_t*>(&ks_lds[buf][r * KSTR + col * 8]) = kpre[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int c = tid + i * NT;
-      if (VTASKS % NT == 0 || c < VTASKS) {
-        const int quad = c / DCH, col = c % DCH;
-        const int slot = vslot(4 * quad);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const int sh = (e & 1) * 16;
-          u32x2_t pk;
-          pk[0] = ((vpre[i][0][w] >> sh) & 0xffffu) | (((vpre[i][1][w] >> sh) & 0xffffu) << 16);
-          pk[1] = ((vpre[i][2][w] >> sh) & 0xffffu) | (((vpre[i][3][w] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(col * 8 + e) * VSTR + slot]) = pk;
-        }
-      }
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      const int vo = voff[i];  // (a local copy: passing voff[i] directly drops the host-side kernel stub)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
     }
   };
 
-  // The loop sits inside this branch so that no path reaches it with the Q
-  // loads still in flight (which would make every iteration wait for all
-  // outstanding loads, prefetch included).  nblocks is uniform over the
-  // workgroup, so the barriers inside are too.
-  if (nblocks > 0) {
-    load_block(0);
-    store_block(0);
-    if (nblocks > 1) load_block(BN);
-    __syncthreads();
-
-  for (int it = 0; it < nblocks; ++it) {
-    const int buf = it & 1;
-    const int kb = it * BN;
-    if (wave_live && kb < wave_kv_end) {
-      // S^T = K Q^T for NS tiles of 32 keys.
-      f32x16_t s[NS];
+  auto compute_block = [&](int kb, const char* buf) {
+    if (!(wave_live && kb < wave_kv_end)) return;
+    const char* kt = buf;
+    const char* vt = buf + TILE;
+    // S^T = K Q^T for NS tiles of 32 keys.
+    // The NS accumulation chains are interleaved, k outermost.
+    f32x16_t s[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
+        const u32x4_t kop = *reinterpret_cast<const u32x4_t*>(kt + 32 * i * RB + koff[k]);
+        s[i] = E::mfma(kop, qv[k], s[i]);
+      }
+    const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
+    if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
+    softmax_step<NS, DT32>(s, acc, m, l, a.scale_log2);
+
+    // O^T += V^T P^T.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
+    for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u32x4_t kop =
-              *reinterpret_cast<const u32x4_t*>(&ks_lds[buf][(32 * i + n) * KSTR + 16 * k + 8 * hh]);
-          s[i] = E::mfma(kop, qv[k], s[i]);
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4_t pop;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pop[j] = E::pack2(s[i][8 * kk + 2 * j], s[i][8 * kk + 2 * j + 1]);
+#pragma unroll
+        for (int d = 0; d < DT32; ++d) {
+          const char* base = vt + (32 * i + 16 * kk) * RB;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VLP_LDS i16x4_t*)(base + vtoff[0][d]));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VLP_LDS i16x4_t*)(base + vtoff[1][d]));
+          u32x4_t vop;
+          vop[0] = __builtin_bit_cast(u32x2_t, lo)[0];
+          vop[1] = __builtin_bit_cast(u32x2_t, lo)[1];
+          vop[2] = __builtin_bit_cast(u32x2_t, hi)[0];
+          vop[3] = __builtin_bit_cast(u32x2_t, hi)[1];
+          acc[d] = E::mfma(vop, pop, acc[d]);
         }
       }
-      const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
-      if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
-      softmax_step<NS, DT32>(s, acc, m, l, a.scale_log2);
+  };
 
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4_t pop;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pop[j] = E::pack2(s[i][8 * kk + 2 * j], s[i][8 * kk + 2 * j + 1]);
-#pragma unroll
-          for (int d = 0; d < DT32; ++d) {
-            const u32x4_t vop = *reinterpret_cast<const u32x4_t*>(
-                &vt_lds[buf][(32 * d + n) * VSTR + 32 * i + 16 * kk + 8 * hh]);
-            acc[d] = E::mfma(vop, pop, acc[d]);
-          }
-        }
-    }
-    if (it + 1 < nblocks) {
-      store_block(buf ^ 1);                         // block it+1, loaded one block ago
-      if (it + 2 < nblocks) load_block((it + 2) * BN);
-    }
+  // nblocks is uniform over the workgroup, so every barrier below is too.
+  if (nblocks > 0) {
+    issue_block(0, lds0);
+    wait_vmem_all();
     __syncthreads();
-  }
+    for (int it = 0; it < nblocks; it += 2) {
+      if (it + 1 < nblocks) issue_block((it + 1) * BN, lds1);
+      compute_block(it * BN, lds0);
+      wait_vmem_all();
+      __syncthreads();
+      if (it + 1 >= nblocks) break;
+      if (it + 2 < nblocks) issue_block((it + 2) * BN, lds0);
+      compute_block((it + 1) * BN, lds1);
+      wait_vmem_all();
+      __syncthreads();
+    }
   }
 
   // Epilogue: normalise, round to the element type, store real rows only.
@@ -403,7 +435,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
     a.lse[static_cast<size_t>(tc.head) * a.rows_q + tc.q_start + my_row] =
         l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : kNegInf;
 }
-
 // ---------------------------------------------------------------------------
 // fp32 inputs
 // ---------------------------------------------------------------------------
