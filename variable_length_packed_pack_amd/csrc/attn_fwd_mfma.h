@@ -118,6 +118,15 @@ __device__ __forceinline__ bool decode_workgroup(const AttnArgs& a, TileCoord& t
   return true;
 }
 
+// Maximum over the two half-waves (lanes i and i + 32): v_permlane32_swap
+// exchanges the halves of two registers in one VALU step, instead of a
+// round trip through the LDS crossbar.
+__device__ __forceinline__ float halves_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 // Online-softmax step for one block of scores held as NS registers of 16
 // values per lane (scores of one query row per lane; see the header comment).
 // The reference max m (log2 units) moves lazily: only when some row of the
@@ -140,7 +149,7 @@ __device__ __forceinline__ void softmax_step(f32x16_t (&s)[NS], f32x16_t (&acc)[
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[i][r]);
   float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = halves_max(mx);
   const float mt = mx * scale_log2;
   if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleLog2)) {
     const float m_new = fmaxf(m, mt);
