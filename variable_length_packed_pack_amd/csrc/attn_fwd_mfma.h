@@ -377,6 +377,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
         const u32x4_t kop = *reinterpret_cast<const u32x4_t*>(kt + 32 * i * RB + koff[k]);
         s[i] = E::mfma(kop, qv[k], s[i]);
       }
+    // Keep the K-operand reads QK_AHEAD MFMAs ahead of their use: an LDS
+    // read takes several MFMA issue slots to return.
+    constexpr int NQK = KS * NS;
+    constexpr int QK_AHEAD = NQK < 4 ? NQK : 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);  // DS reads
+#pragma unroll
+    for (int t = 0; t < NQK; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (t + QK_AHEAD < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+    }
     const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
     if (need_mask) mask_scores<NS, CAUSAL>(s, kb, hh, tc.lk, my_row, diag);
     softmax_step<NS, DT32>(s, acc, m, l, a.scale_log2);
