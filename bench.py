@@ -57,16 +57,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_flops(lengths: np.ndarray, heads: int, head_dim: int, causal: bool) -> float:
-    """4 * sum N_i^2 * H * D, halved when causal."""
+def algorithmic_flops(lengths: np.ndarray, heads: int, head_dim: int, causal: bool,
+                      first_token: bool = False) -> float:
+    """4 * sum N_i^2 * H * D, halved when causal; 4 * sum N_i * H * D with
+    one query per sequence (a causal first token sees one key)."""
+    if first_token:
+        keys = float(len(lengths)) if causal else float(np.sum(lengths.astype(np.float64)))
+        return 4.0 * keys * heads * head_dim
     n2 = float(np.sum(lengths.astype(np.float64) ** 2))
     f = 4.0 * n2 * heads * head_dim
     return f / 2 if causal else f
 
 
-def compulsory_bytes(total: int, heads: int, head_dim: int, elt: int) -> float:
+def compulsory_bytes(rows_q: int, total_k: int, heads: int, head_dim: int, elt: int) -> float:
     """q, k, v read once, out written once, lse written once."""
-    return 4.0 * total * heads * head_dim * elt + 4.0 * total * heads
+    return (2.0 * rows_q + 2.0 * total_k) * heads * head_dim * elt + 4.0 * rows_q * heads
 
 
 def traffic_from_profile(workload: str, src_hash: str):
@@ -82,24 +87,28 @@ def traffic_from_profile(workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_oracle_baseline(wl, budget_s: float):
+def cpu_oracle_baseline(wl, budget_s: float, first_token: bool = False):
     """Time the oracle on a bounded sample of the same batch: whole heads (every
     sequence of the batch for that head), one after another, until the
     elapsed time reaches the budget (at least one head)."""
     import oracle  # test infrastructure: used only for this reported baseline
 
     cu = wl.cu_seqlens_host()
+    rows = cu[:-1].astype(np.int64)
     elapsed, heads_done = 0.0, 0
     while heads_done < wl.heads and (heads_done == 0 or elapsed < budget_s):
         hh = heads_done
         q = wl.q[:, hh:hh + 1].float().numpy()
         k = wl.k[:, hh:hh + 1].float().numpy()
         v = wl.v[:, hh:hh + 1].float().numpy()
+        if first_token:
+            q = q[rows]
         t0 = time.perf_counter()
-        oracle.varlen_attention(q, k, v, cu, cu, wl.scale, wl.causal)
+        oracle.varlen_attention(q, k, v, None if first_token else cu, cu, wl.scale, wl.causal,
+                                query_is_first_token=first_token)
         elapsed += time.perf_counter() - t0
         heads_done += 1
-    flops = algorithmic_flops(wl.lengths, heads_done, wl.head_dim, wl.causal)
+    flops = algorithmic_flops(wl.lengths, heads_done, wl.head_dim, wl.causal, first_token=first_token)
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -118,9 +127,10 @@ def cpu_oracle_baseline(wl, budget_s: float):
     }
 
 
-def padded_comparator(wl, q, k, v, reps: int):
+def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
     """torch SDPA over the padded envelope [B, H, L_max, D] (same data),
-    chunked over the batch if the envelope is large; returns (ms, backend)."""
+    chunked over the batch if the envelope is large; returns (ms, backend).
+    In first-token mode q is [B, H, D] and the padded query is [B, H, 1, D]."""
     import torch
     from torch.nn.attention import SDPBackend, sdpa_kernel
 
@@ -135,12 +145,13 @@ def padded_comparator(wl, q, k, v, reps: int):
     for c0 in range(0, b, chunk):
         c1 = min(b, c0 + chunk)
         nb = c1 - c0
-        qp = torch.zeros(nb, h, lmax, d, dtype=q.dtype, device=q.device)
-        kp = torch.zeros_like(qp)
-        vp = torch.zeros_like(qp)
+        kp = torch.zeros(nb, h, lmax, d, dtype=q.dtype, device=q.device)
+        vp = torch.zeros_like(kp)
+        qp = q[c0:c1].unsqueeze(2).contiguous() if first_token else torch.zeros_like(kp)
         for j, i in enumerate(range(c0, c1)):
             s, e = int(cu[i]), int(cu[i + 1])
-            qp[j, :, : e - s] = q[s:e].transpose(0, 1)
+            if not first_token:
+                qp[j, :, : e - s] = q[s:e].transpose(0, 1)
             kp[j, :, : e - s] = k[s:e].transpose(0, 1)
             vp[j, :, : e - s] = v[s:e].transpose(0, 1)
         mask = None
@@ -189,6 +200,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
+    ap.add_argument("--first-token", action="store_true",
+                    help="query_is_first_token mode: one query per sequence (its first token)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
                          "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -221,14 +234,19 @@ def main() -> int:
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)
+    ft = args.first_token
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
     t, h, d = wl.total_tokens, wl.heads, wl.head_dim
     b = wl.num_seqs
-    flops = algorithmic_flops(wl.lengths, h, d, wl.causal)
+    if ft:
+        # one query per sequence: the row cu_seqlens[i] of the packed batch
+        q = q[torch.from_numpy(wl.cu_seqlens_host()[:-1]).long().to(dev)].contiguous()
+    rows_q = q.shape[0]
+    flops = algorithmic_flops(wl.lengths, h, d, wl.causal, first_token=ft)
     out = torch.empty_like(q)
-    lse = torch.empty(h, t, dtype=torch.float32, device=dev)
-    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, False, b, t, wl.max_len)
-    ws = torch.empty(vlp.workspace_size(b, t, bm), dtype=torch.uint8, device=dev)
+    lse = torch.empty(h, rows_q, dtype=torch.float32, device=dev)
+    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, ft, b, rows_q, wl.max_len)
+    ws = torch.empty(vlp.workspace_size(b, rows_q, bm), dtype=torch.uint8, device=dev)
     cu_dev = torch.empty(b + 1, dtype=torch.int32, device=dev)
     lengths_host = wl.lengths.copy()
     n_steps = args.warmup + args.steps
@@ -238,7 +256,7 @@ def main() -> int:
         flat, cu = vlp.pack_sequences(lengths_host, wl.max_len)
         pinned[i].copy_(cu)
         cu_dev.copy_(pinned[i], non_blocking=True)
-        vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+        vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                             workspace=ws)
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -268,12 +286,12 @@ def main() -> int:
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(3):
-            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                                 grid=grid)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for _ in range(reps):
-            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, False, out=out, lse=lse,
+            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                                 grid=grid)
         ev1.record(stream)
     stream.synchronize()
@@ -281,23 +299,31 @@ def main() -> int:
     torch.cuda.synchronize()
 
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[wl.dtype]
-    src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(args.workload, src_hash)
     elt = q.element_size()
+    nbytes = compulsory_bytes(rows_q, t, h, d, elt)
+    if ft:
+        # one query per sequence streams all of K and V: bandwidth-bound
+        roof = {"bound": "hbm", "achieved": round(nbytes / (kernel_ms * 1e-3) / 1e9, 3), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / (kernel_ms * 1e-3) / 1e12, 3),
+                "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = None if ft else traffic_from_profile(args.workload, src_hash)
     log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
 
     padded_ms, padded_backend = (None, "skipped")
     if not args.no_padded:
         log("[bench] padded SDPA comparator")
-        padded_ms, padded_backend = padded_comparator(wl, q, k, v, reps=3)
+        padded_ms, padded_backend = padded_comparator(wl, q, k, v, reps=3, first_token=ft)
     torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        cpu = cpu_oracle_baseline(wl, args.cpu_budget)
+        cpu = cpu_oracle_baseline(wl, args.cpu_budget, first_token=ft)
 
     lmax = wl.max_len
     rec = {
@@ -328,24 +354,19 @@ def main() -> int:
             "heads": h,
             "head_dim": d,
             "causal": wl.causal,
+            "query_is_first_token": ft,
             "block_m": bm,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-        },
+        "roofline": {**roof, "traffic": traffic},
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
         "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
         "padded_ms": None if padded_ms is None else round(padded_ms, 3),
         "padded_backend": padded_backend,
         "kernel_ms": round(kernel_ms, 4),
+        "kernel_tflops": round(achieved, 3),
         "kernel_source_hash": src_hash,
         "algorithmic_gflop": round(flops / 1e9, 3),
-        "compulsory_gb": round(compulsory_bytes(t, h, d, elt) / 1e9, 4),
+        "compulsory_gb": round(nbytes / 1e9, 4),
         "rho_seq": round(t / (b * lmax), 4),
         "work_ratio": round(float(np.sum(wl.lengths.astype(np.float64) ** 2)) / (b * lmax * lmax), 5),
         "pack_sequences_host_us": round(pack_us, 1),
