@@ -4,14 +4,16 @@
 // list is a prefix sum of per-sequence tile counts, sized on the host by
 // G_cap).
 //
-// One workgroup of 1024 threads:
+// One workgroup of 256 threads (four waves); the sequence lengths are read
+// from HBM once and kept in LDS:
 //   1. tile counts ceil(len_i / block_m) and their exclusive prefix sum
-//      (each thread scans a contiguous chunk of sequences; the chunk totals
-//      are scanned in LDS) -> block_offsets, and grid_mapping filled per
-//      sequence;
-//   2. longest-first order: a bitonic sort in LDS of the 64-bit keys
-//      ((INT32_MAX - len) << 32 | i), which orders by length descending with
-//      ties to the lower index -- the same order as a stable sort by length;
+//      (each thread sums a contiguous chunk of sequences; chunk totals are
+//      scanned within each wave by lane shuffles, then across the four
+//      waves) -> block_offsets, and grid_mapping filled per sequence;
+//   2. longest-first order (length descending, ties to the lower index, the
+//      order of a stable sort by length): for up to kRankMax sequences every
+//      sequence counts the sequences that precede it; above that, a bitonic
+//      sort in LDS of the keys ((INT32_MAX - len) << 32 | i);
 //   3. a second prefix sum of tile counts in that order gives every
 //      sequence's position in tile_order, filled last tile first.
 // Entries from G to grid_cap are set to -1.
@@ -23,7 +25,9 @@
 namespace vlp {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRankMax = 256;  // rank counting below this many sequences, bitonic sort above
 
 __device__ __forceinline__ int tiles_for(int len, int block_m) {
   return len <= 0 ? 0 : 1 + (len - 1) / block_m;
@@ -31,29 +35,38 @@ __device__ __forceinline__ int tiles_for(int len, int block_m) {
 
 // Exclusive scan of one value per thread over the workgroup; returns the
 // thread's exclusive prefix and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int* part, int* total) {
-  const int tid = threadIdx.x;
-  part[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
+__device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
   }
-  const int incl = part[tid];
-  *total = part[kThreads - 1];
+  if (lane == 63) wave_sums[w] = incl;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int x = wave_sums[i];
+    base += i < w ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  __syncthreads();  // wave_sums may be reused by the next scan
+  return base + incl - v;
 }
 
 __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __restrict__ cu, int num_seqs,
                                                               int block_m, int32_t* __restrict__ block_offsets,
                                                               int32_t* __restrict__ grid_mapping,
                                                               int32_t* __restrict__ tile_order, int grid_cap) {
-  __shared__ int part[kThreads];
+  __shared__ int len_s[VLP_DEVICE_SORT_MAX_SEQS];
+  __shared__ int bo_s[VLP_DEVICE_SORT_MAX_SEQS];
+  __shared__ int order_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ unsigned long long keys[VLP_DEVICE_SORT_MAX_SEQS];
-  __shared__ int bo_lds[VLP_DEVICE_SORT_MAX_SEQS];
+  __shared__ int wave_sums[kWaves];
   const int tid = threadIdx.x;
   const int per = (num_seqs + kThreads - 1) / kThreads;
   const int beg = min(num_seqs, tid * per);
@@ -62,13 +75,17 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
 
   // 1. block_offsets and grid_mapping.
   int local = 0;
-  for (int i = beg; i < end; ++i) local += tiles_for(cu[i + 1] - cu[i], block_m);
-  int g = 0;
-  int run = block_exclusive_scan(local, part, &g);
   for (int i = beg; i < end; ++i) {
-    const int nt = tiles_for(cu[i + 1] - cu[i], block_m);
+    const int len = cu[i + 1] - cu[i];
+    if (sorted) len_s[i] = len;
+    local += tiles_for(len, block_m);
+  }
+  int g = 0;
+  int run = block_exclusive_scan(local, wave_sums, &g);
+  for (int i = beg; i < end; ++i) {
+    const int nt = tiles_for(sorted ? len_s[i] : cu[i + 1] - cu[i], block_m);
     block_offsets[i] = run;
-    if (sorted) bo_lds[i] = run;
+    if (sorted) bo_s[i] = run;
     for (int t = 0; t < nt; ++t)
       if (run + t < grid_cap) grid_mapping[run + t] = i;
     run += nt;
@@ -83,49 +100,61 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
     for (int f = tid; f < g && f < grid_cap; f += kThreads) tile_order[f] = f;
     return;
   }
+  __syncthreads();  // len_s and bo_s complete
 
-  // 2. bitonic sort of (length descending, index ascending).
-  int p2 = 1;
-  while (p2 < num_seqs) p2 <<= 1;
-  for (int i = tid; i < p2; i += kThreads) {
-    if (i < num_seqs) {
-      const unsigned len = static_cast<unsigned>(cu[i + 1] - cu[i]);
-      keys[i] = (static_cast<unsigned long long>(0x7fffffffu - len) << 32) | static_cast<unsigned>(i);
-    } else {
-      keys[i] = ~0ull;
+  // 2. the longest-first order: order_s[r] = the sequence at rank r.
+  if (num_seqs <= kRankMax) {
+    for (int i = tid; i < num_seqs; i += kThreads) {
+      const int li = len_s[i];
+      int rank = 0;
+      for (int j = 0; j < num_seqs; ++j) {
+        const int lj = len_s[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      order_s[rank] = i;
     }
-  }
-  __syncthreads();
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < p2; i += kThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = keys[i], y = keys[ixj];
-          const bool ascending = (i & k) == 0;
-          if ((x > y) == ascending) {
-            keys[i] = y;
-            keys[ixj] = x;
+  } else {
+    int p2 = 1;
+    while (p2 < num_seqs) p2 <<= 1;
+    for (int i = tid; i < p2; i += kThreads) {
+      if (i < num_seqs) {
+        const unsigned len = static_cast<unsigned>(len_s[i]);
+        keys[i] = (static_cast<unsigned long long>(0x7fffffffu - len) << 32) | static_cast<unsigned>(i);
+      } else {
+        keys[i] = ~0ull;
+      }
+    }
+    __syncthreads();
+    for (int k = 2; k <= p2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < p2; i += kThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long x = keys[i], y = keys[ixj];
+            const bool ascending = (i & k) == 0;
+            if ((x > y) == ascending) {
+              keys[i] = y;
+              keys[ixj] = x;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
+    for (int r = tid; r < num_seqs; r += kThreads) order_s[r] = static_cast<int>(keys[r] & 0xffffffffu);
   }
+  __syncthreads();
 
   // 3. positions in the longest-first order, then the tiles of each sequence
   // from its last local tile down to tile 0.
   local = 0;
-  for (int r = beg; r < end; ++r) {
-    const int i = static_cast<int>(keys[r] & 0xffffffffu);
-    local += tiles_for(cu[i + 1] - cu[i], block_m);
-  }
+  for (int r = beg; r < end; ++r) local += tiles_for(len_s[order_s[r]], block_m);
   int dummy = 0;
-  int pos = block_exclusive_scan(local, part, &dummy);
+  int pos = block_exclusive_scan(local, wave_sums, &dummy);
   for (int r = beg; r < end; ++r) {
-    const int i = static_cast<int>(keys[r] & 0xffffffffu);
-    const int nt = tiles_for(cu[i + 1] - cu[i], block_m);
-    const int first = bo_lds[i];
+    const int i = order_s[r];
+    const int nt = tiles_for(len_s[i], block_m);
+    const int first = bo_s[i];
     for (int u = 0; u < nt; ++u)
       if (pos + u < grid_cap) tile_order[pos + u] = first + nt - 1 - u;
     pos += nt;
