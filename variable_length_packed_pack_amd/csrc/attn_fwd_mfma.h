@@ -456,28 +456,52 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
 }
 // ---------------------------------------------------------------------------
 // fp32 inputs
+//
+// Same tile structure as the 16-bit path -- row-major K and V tiles filled
+// by direct buffer-to-LDS loads (zeros past the sequence end), two LDS
+// buffers, one barrier per key block -- with v_mfma_f32_32x32x2_f32, whose
+// A and B operands are one element per lane (k = hh).  S^T = K Q^T: the
+// contraction index d is split as d = hh*D/2 + step, so a lane keeps half of
+// its query row and reads 16-byte K chunks.  O^T = V^T P^T: one key pair per
+// MFMA, so each V^T operand is a single 4-byte read and V needs no
+// transpose.  The chunk swizzle makes the K reads (16 consecutive rows, one
+// chunk) and the V reads (32 consecutive columns of rows k and k+4) free of
+// bank conflicts for rows of 256 bytes and more.
 // ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int chunk_swz_f32(int row) {
+  if constexpr (D >= 64) {
+    return (row & 3) | ((row & 4) << 1) | ((row & 8) >> 1);
+  } else {
+    return 0;
+  }
+}
+
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   static_assert(D % 16 == 0, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int HALF = D / 2;                   // d-values per half-wave
-  constexpr int DT32 = (D + 31) / 32;
-  constexpr int NS = BN / 32;
-  constexpr int STR = D + 4;                    // row stride (floats)
-  constexpr int DCH = D / 4;                    // 16-byte chunks per row
+  constexpr int HALF = D / 2;           // d-values per half-wave
+  constexpr int DT32 = (D + 31) / 32;   // 32-wide output column tiles
+  constexpr int NS = BN / 32;           // 32-key score tiles per block
+  constexpr int RB = D * 4;             // bytes per tile row
+  constexpr int CPR = D / 4;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows filled by one 1 KB direct load
+  constexpr int LPT = BN / RPI;         // direct loads per tile
+  static_assert(LPT % NW == 0, "tile loads must split evenly over the waves");
+  constexpr int LPW = LPT / NW;
+  constexpr int TILE = BN * RB;
 
-  __shared__ __attribute__((aligned(16))) float ks_lds[BN * STR];
-  __shared__ __attribute__((aligned(16))) float vs_lds[BN * STR];
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
 
   TileCoord tc;
   if (!decode_workgroup(a, tc)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int row0 = tc.tile * BM;
@@ -486,7 +510,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const size_t rs = static_cast<size_t>(a.heads) * D;
+  const int rs_bytes = a.heads * D * 4;
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -496,16 +520,33 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
   int wave_kv_end = tc.lk;
   if (CAUSAL) wave_kv_end = min(tc.lk, min(wrow0 + 32, tc.lq) + diag);
 
-  // Q^T operand: contraction index d is split as d = hh * D/2 + step, so a
-  // lane keeps the half hh of its query row.
+  // Q^T operand: half hh of this lane's query row (rows past the sequence
+  // end load the last real row; their results are never stored).
   f32x4_t qv[HALF / 4];
   {
+    const int qrow = min(my_row, tc.lq - 1);
     const float* qp = static_cast<const float*>(a.q) +
-                      (static_cast<size_t>(tc.q_start + my_row) * a.heads + tc.head) * D + hh * HALF;
+                      (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D + hh * HALF;
 #pragma unroll
-    for (int j = 0; j < HALF / 4; ++j)
-      qv[j] = row_ok ? *reinterpret_cast<const f32x4_t*>(qp + 4 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < HALF / 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(qp + 4 * j);
   }
+
+  // Direct-load lane offsets (see the 16-bit path).
+  int voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = wave * LPW + i;
+    const int r = j * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ chunk_swz_f32<D>(r);
+    voff[i] = r * rs_bytes + c * 16;
+  }
+  // K operand chunks: row 32i+n, logical chunk hh*HALF/4 + j.
+  int koff[HALF / 4];
+#pragma unroll
+  for (int j = 0; j < HALF / 4; ++j) koff[j] = n * RB + (((hh * (HALF / 4) + j) ^ chunk_swz_f32<D>(n)) << 4);
+  // V^T operand: row key, column 32d + n; the row's swizzle depends on key & 15,
+  // which is 8(r>>2) + 4hh + (r&3) for score register r.
+  const int vcol_chunk = n >> 2, vcol_byte = (n & 3) * 4;
 
   f32x16_t acc[DT32];
 #pragma unroll
@@ -515,25 +556,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
   float m = kNegInf;
   float l = 0.0f;
 
-  const float* kbase = static_cast<const float*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * D;
-  const float* vbase = static_cast<const float*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * D;
+  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
+  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
 
-  for (int it = 0; it < nblocks; ++it) {
-    const int kb = it * BN;
-    __syncthreads();
-    for (int c = tid; c < BN * DCH; c += NT) {
-      const int r = c / DCH, col = c - (c / DCH) * DCH;
-      f32x4_t kv = f32x4_t{0.f, 0.f, 0.f, 0.f}, vv = kv;
-      if (kb + r < tc.lk) {
-        kv = *reinterpret_cast<const f32x4_t*>(kbase + (size_t)(kb + r) * rs + col * 4);
-        vv = *reinterpret_cast<const f32x4_t*>(vbase + (size_t)(kb + r) * rs + col * 4);
-      }
-      *reinterpret_cast<f32x4_t*>(&ks_lds[r * STR + col * 4]) = kv;
-      *reinterpret_cast<f32x4_t*>(&vs_lds[r * STR + col * 4]) = vv;
+  auto issue_block = [&](int kb, char* buf) {
+    const int nrows = min(BN, tc.lk - kb);
+    const int nrec = (nrows - 1) * rs_bytes + RB;
+    const size_t boff = static_cast<size_t>(kb) * rs_bytes;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kseq + boff), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vseq + boff), 0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      const int vo = voff[i];  // (a local copy: passing voff[i] directly drops the host-side kernel stub)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
     }
-    __syncthreads();
-    if (!wave_live || kb >= wave_kv_end) continue;
+  };
 
+  auto compute_block = [&](int kb, const char* buf) {
+    if (!(wave_live && kb < wave_kv_end)) return;
+    const char* kt = buf;
+    const char* vt = buf + TILE;
     f32x16_t s[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -541,7 +585,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
       for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
 #pragma unroll
       for (int j = 0; j < HALF / 4; ++j) {
-        const f32x4_t kop = *reinterpret_cast<const f32x4_t*>(&ks_lds[(32 * i + n) * STR + hh * HALF + 4 * j]);
+        const f32x4_t kop = *reinterpret_cast<const f32x4_t*>(kt + 32 * i * RB + koff[j]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[e], qv[j][e], s[i], 0, 0, 0);
       }
@@ -557,12 +601,33 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_f32(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const char* vrow = vt + key * RB;
+        const int sw = chunk_swz_f32<D>(key);
 #pragma unroll
         for (int d = 0; d < DT32; ++d) {
-          const float vop = (32 * d + n < D) ? vs_lds[key * STR + 32 * d + n] : 0.0f;
+          const float vop = (32 * d + n < D)
+                                ? *reinterpret_cast<const float*>(vrow + (((8 * d + vcol_chunk) ^ sw) << 4) + vcol_byte)
+                                : 0.0f;
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, s[i][r], acc[d], 0, 0, 0);
         }
       }
+  };
+
+  if (nblocks > 0) {
+    issue_block(0, lds0);
+    wait_vmem_all();
+    __syncthreads();
+    for (int it = 0; it < nblocks; it += 2) {
+      if (it + 1 < nblocks) issue_block((it + 1) * BN, lds1);
+      compute_block(it * BN, lds0);
+      wait_vmem_all();
+      __syncthreads();
+      if (it + 1 >= nblocks) break;
+      if (it + 2 < nblocks) issue_block((it + 2) * BN, lds0);
+      compute_block((it + 1) * BN, lds1);
+      wait_vmem_all();
+      __syncthreads();
+    }
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
