@@ -201,7 +201,8 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  *   heads, head_dim  heads >= 1; head_dim in {16, 32, 64, 128} ("head_dim must
  *                  be a multiple of 8"; these four are built).
  *   max_seqlen     a hint (0 = unknown); never needed for correctness.
- *   scale          finite softmax scale (usually 1/sqrt(head_dim)).
+ *   scale          finite softmax scale >= 0 (usually 1/sqrt(head_dim)); the
+ *                  running row maximum is taken on the unscaled scores.
  *   causal         0/1: key j of a sequence is visible to its query at local
  *                  position p iff j <= p + (Lk - Lq) (bottom-right aligned).
  *   query_is_first_token  0/1: one query per sequence, at local position 0.
@@ -215,7 +216,7 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  * Errors: NULL q/k/v/out/cu_seqlens_k/workspace (or cu_seqlens_q outside
  * first-token mode) -> VLP_ERR_NULL; dtype or head_dim not built ->
  * VLP_ERR_UNSUPPORTED; num_seqs < 1, heads < 1, rows_q < 0, total_k < 0,
- * non-finite scale, misaligned pointers, rows_q != num_seqs in first-token
+ * non-finite or negative scale, misaligned pointers, rows_q != num_seqs in first-token
  * mode -> VLP_ERR_INVALID; rows or rows*heads beyond int32 -> VLP_ERR_OVERFLOW;
  * small workspace -> VLP_ERR_CAPACITY; launch failure -> VLP_ERR_HIP.
  */

@@ -223,6 +223,8 @@ def test_forward_validation_errors():
     assert _fwd(rows_q=-1) == 2
     assert _fwd(scale=float("nan")) == 2
     assert _fwd(scale=float("inf")) == 2
+    assert _fwd(scale=-0.125) == 2  # the online max assumes a non-negative scale
+    assert _fwd(scale=0.0) != 2
     assert _fwd(q=FAKE + 8) == 2
     assert _fwd(out=FAKE + 4) == 2
     assert _fwd(ws=FAKE + 16) == 2
@@ -237,7 +239,7 @@ def test_grid_forward_validation_errors():
     lib = _lib.load()
 
     def call(**kw):
-        a = dict(gm=FAKE, bo=FAKE, to=None, nb=3, bm=128, head_dim=128)
+        a = dict(gm=FAKE, bo=FAKE, to=None, nb=3, bm=lib.vlp_kernel_block_m(2, 128, 0, 0, 4, 100, 0), head_dim=128)
         a.update(kw)
         return lib.vlp_varlen_attn_fwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, a["head_dim"], 0,
                                             0.1, 0, 0, FAKE, None, a["gm"], a["bo"], a["to"], a["nb"], a["bm"],

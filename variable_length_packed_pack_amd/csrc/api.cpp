@@ -58,7 +58,7 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
   if (!vlp::head_dim_built(head_dim)) return VLP_ERR_UNSUPPORTED;
   if (num_seqs < 1 || heads < 1 || rows_q < 0 || total_k < 0 || max_seqlen < 0) return VLP_ERR_INVALID;
   if ((causal != 0 && causal != 1) || (first_token != 0 && first_token != 1)) return VLP_ERR_INVALID;
-  if (!isfinite(scale)) return VLP_ERR_INVALID;
+  if (!isfinite(scale) || scale < 0.0f) return VLP_ERR_INVALID;  // the online max assumes scale >= 0
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VLP_ERR_INVALID;
   if (first_token && rows_q != num_seqs) return VLP_ERR_INVALID;
   if (rows_q > INT32_MAX || total_k > INT32_MAX) return VLP_ERR_OVERFLOW;
