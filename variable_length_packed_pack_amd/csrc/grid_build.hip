@@ -9,13 +9,15 @@
 //   1. tile counts ceil(len_i / block_m) and their exclusive prefix sum
 //      (each thread sums a contiguous chunk of sequences; chunk totals are
 //      scanned within each wave by lane shuffles, then across the four
-//      waves) -> block_offsets, and grid_mapping filled per sequence;
+//      waves) -> block_offsets; grid_mapping one tile per thread, by a
+//      binary search of the offsets;
 //   2. longest-first order (length descending, ties to the lower index, the
 //      order of a stable sort by length): for up to kRankMax sequences every
 //      sequence counts the sequences that precede it; above that, a bitonic
 //      sort in LDS of the keys ((INT32_MAX - len) << 32 | i);
 //   3. a second prefix sum of tile counts in that order gives every
-//      sequence's position in tile_order, filled last tile first.
+//      sequence's position in tile_order; each slot is filled by its own
+//      thread (binary search of the positions), last tile first.
 // Entries from G to grid_cap are set to -1.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
   __shared__ int len_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int bo_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int order_s[VLP_DEVICE_SORT_MAX_SEQS];
+  __shared__ int pos_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ unsigned long long keys[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int wave_sums[kWaves];
   const int tid = threadIdx.x;
@@ -82,25 +85,43 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
   }
   int g = 0;
   int run = block_exclusive_scan(local, wave_sums, &g);
-  for (int i = beg; i < end; ++i) {
-    const int nt = tiles_for(sorted ? len_s[i] : cu[i + 1] - cu[i], block_m);
-    block_offsets[i] = run;
-    if (sorted) bo_s[i] = run;
-    for (int t = 0; t < nt; ++t)
-      if (run + t < grid_cap) grid_mapping[run + t] = i;
-    run += nt;
-  }
-  if (tid == 0) block_offsets[num_seqs] = g;
-  for (int f = g + tid; f < grid_cap; f += kThreads) {
-    grid_mapping[f] = -1;
-    tile_order[f] = -1;
-  }
-
   if (!sorted) {
-    for (int f = tid; f < g && f < grid_cap; f += kThreads) tile_order[f] = f;
+    for (int i = beg; i < end; ++i) {
+      const int nt = tiles_for(cu[i + 1] - cu[i], block_m);
+      block_offsets[i] = run;
+      for (int t = 0; t < nt; ++t)
+        if (run + t < grid_cap) grid_mapping[run + t] = i;
+      run += nt;
+    }
+    if (tid == 0) block_offsets[num_seqs] = g;
+    for (int f = g + tid; f < grid_cap; f += kThreads) grid_mapping[f] = -1;
+    for (int f = tid; f < grid_cap; f += kThreads) tile_order[f] = f < g ? f : -1;
     return;
   }
+  for (int i = beg; i < end; ++i) {
+    bo_s[i] = run;
+    block_offsets[i] = run;
+    run += tiles_for(len_s[i], block_m);
+  }
+  if (tid == 0) block_offsets[num_seqs] = g;
   __syncthreads();  // len_s and bo_s complete
+
+  // grid_mapping, one tile per thread: the owner of tile f is the last
+  // sequence that starts at or before f (empty sequences start where the
+  // next one does and own nothing).
+  const int gw = min(g, grid_cap);
+  for (int f = tid; f < grid_cap; f += kThreads) {
+    int owner = -1;
+    if (f < gw) {
+      int lo = 0, hi = num_seqs - 1;  // bo_s[0] = 0 <= f
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bo_s[mid] <= f) lo = mid; else hi = mid - 1;
+      }
+      owner = lo;
+    }
+    grid_mapping[f] = owner;
+  }
 
   // 2. the longest-first order: order_s[r] = the sequence at rank r.
   if (num_seqs <= kRankMax) {
@@ -145,20 +166,30 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
   }
   __syncthreads();
 
-  // 3. positions in the longest-first order, then the tiles of each sequence
-  // from its last local tile down to tile 0.
+  // 3. positions in the longest-first order (pos_s[r] = first slot of the
+  // sequence at rank r), then one slot per thread: slot p belongs to the
+  // last rank whose position is <= p and takes that sequence's tiles from
+  // its last local tile down to tile 0.
   local = 0;
   for (int r = beg; r < end; ++r) local += tiles_for(len_s[order_s[r]], block_m);
   int dummy = 0;
   int pos = block_exclusive_scan(local, wave_sums, &dummy);
   for (int r = beg; r < end; ++r) {
-    const int i = order_s[r];
-    const int nt = tiles_for(len_s[i], block_m);
-    const int first = bo_s[i];
-    for (int u = 0; u < nt; ++u)
-      if (pos + u < grid_cap) tile_order[pos + u] = first + nt - 1 - u;
-    pos += nt;
+    pos_s[r] = pos;
+    pos += tiles_for(len_s[order_s[r]], block_m);
   }
+  __syncthreads();
+  for (int p = tid; p < gw; p += kThreads) {
+    int lo = 0, hi = num_seqs - 1;  // pos_s[0] = 0 <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pos_s[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const int i = order_s[lo];
+    const int nt = tiles_for(len_s[i], block_m);
+    tile_order[p] = bo_s[i] + nt - 1 - (p - pos_s[lo]);
+  }
+  for (int p = gw + tid; p < grid_cap; p += kThreads) tile_order[p] = -1;
 }
 
 }  // namespace
