@@ -20,6 +20,12 @@ definition from the pages:
                              per sequence); "gigl.nn.packed_attention" (each
                              sequence attends only to itself; first-token
                              queries).
+* ``varlen_attention_bwd`` -- the gradient of ``varlen_attention`` (no first-
+                             token mode) with respect to q, k and v; the pages
+                             train through the packed attention
+                             ("gigl.nn.packed_attention", "Why this exists";
+                             "DanLing NestedTensor" 3.4) but give no backward
+                             algorithm, so this is the derivative written out.
 
 All pins are in ``tests/test_oracle.py``; no oracle function is "parity unpinned".
 """
@@ -31,5 +37,7 @@ from .varlen_oracle import (  # noqa: F401
     grid_capacity,
     pack_sequences,
     varlen_attention,
+    varlen_attention_bwd,
+    varlen_attention_bwd_rows,
     varlen_attention_rows,
 )

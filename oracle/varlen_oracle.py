@@ -278,3 +278,129 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
         outs.append(o[0])
         lses.append(l[0])
     return np.asarray(outs), np.asarray(lses)
+
+
+# ---------------------------------------------------------------------------
+# Gradients ("gigl.nn.packed_attention", "Why this exists": training takes the
+# gradients of the same packed attention; "So you wanna CUDA Graph",
+# "Correctness tangent": gradients of inactive rows may stay undefined;
+# "DanLing NestedTensor" 3.4 and 4: gradients flow through the packed payload
+# and are checked at the same precision)
+#
+# The pages define no backward algorithm of their own, so the oracle is the
+# gradient of the forward definition written out.  For one sequence and head,
+# with P the softmax weights (zero for invisible keys) and dO the incoming
+# gradient of the output:
+#   dV = P^T dO
+#   dP = dO V^T
+#   dS = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied row-wise)
+#   dQ = scale * dS K,   dK = scale * dS^T Q
+# A query that sees no key has P = 0, hence zero dQ and no contribution to
+# dK or dV.
+# ---------------------------------------------------------------------------
+
+def _attend_one_bwd(qi, ki, vi, doi, scale: float, causal: bool, positions, lq: int):
+    """Gradients of sum(dO * softmax(scale q k^T) v) for one sequence and head.
+
+    qi / doi [Rq, D] are the query rows at local positions ``positions``
+    (Lq = lq) and their output gradients; ki / vi [Lk, D].  Returns
+    (dq [Rq, D], dk [Lk, D], dv [Lk, D]); dk and dv only hold the
+    contributions of the given query rows.
+    """
+    lk = ki.shape[0]
+    rq = qi.shape[0]
+    dq = np.zeros((rq, qi.shape[1]))
+    dk = np.zeros((lk, ki.shape[1]))
+    dv = np.zeros((lk, vi.shape[1]))
+    if lk == 0 or rq == 0:
+        return dq, dk, dv
+    vis = _visibility(positions, lq, lk, causal)
+    scores = scale * (qi @ ki.T)
+    live = vis.any(axis=1)
+    m = np.where(vis, scores, -np.inf).max(axis=1)
+    m_safe = np.where(live, m, 0.0)
+    w = np.where(vis, np.exp(scores - m_safe[:, None]), 0.0)
+    den = w.sum(axis=1)
+    p = np.zeros_like(w)
+    p[live] = w[live] / den[live, None]                   # softmax weights
+    dv = p.T @ doi
+    dp = doi @ vi.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ ki)
+    dk = scale * (ds.T @ qi)
+    return dq, dk, dv
+
+
+def varlen_attention_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale: float,
+                         causal: bool = False):
+    """Gradients of packed attention with respect to q, k and v.
+
+    Same conventions as ``varlen_attention`` (no first-token mode): q / dout
+    [rows_q, H, D], k / v [T_k, H, D].  Returns (dq [rows_q, H, D],
+    dk [T_k, H, D], dv [T_k, H, D]) in float64; rows owned by no sequence stay
+    zero (the GPU never writes them).
+    """
+    q64, k64, v64, do64 = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+    heads = q64.shape[1]
+    dq = np.zeros(q64.shape)
+    dk = np.zeros(k64.shape)
+    dv = np.zeros(v64.shape)
+    for i in range(len(cu_k) - 1):
+        q0, q1 = cu_q[i], cu_q[i + 1]
+        k0, k1 = cu_k[i], cu_k[i + 1]
+        positions = list(range(q1 - q0))
+        for h in range(heads):
+            a, b, c = _attend_one_bwd(q64[q0:q1, h], k64[k0:k1, h], v64[k0:k1, h], do64[q0:q1, h],
+                                      float(scale), causal, positions, q1 - q0)
+            dq[q0:q1, h] = a
+            dk[k0:k1, h] = b
+            dv[k0:k1, h] = c
+    return dq, dk, dv
+
+
+def varlen_attention_bwd_rows(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale: float,
+                              causal: bool, q_samples, k_samples):
+    """The same gradients at sampled rows, for checks at full workload sizes.
+
+    ``q_samples``: (packed query row, head) pairs -> dq rows (one query row at
+    a time: dq of a row depends on that row only).  ``k_samples``: (packed key
+    row, head) pairs -> dk and dv rows; every query of the key's sequence
+    contributes, so the whole (sequence, head) is evaluated once per distinct
+    pair.  Returns (dq [n_q, D], dk [n_k, D], dv [n_k, D]) in float64.
+    """
+    cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
+
+    def owner(cu, row):
+        for i in range(len(cu) - 1):
+            if cu[i] <= row < cu[i + 1]:
+                return i
+        raise ValueError(f"row {row} belongs to no sequence")
+
+    dqs = []
+    for row, h in q_samples:
+        i = owner(cu_q, row)
+        k0, k1 = cu_k[i], cu_k[i + 1]
+        a, _, _ = _attend_one_bwd(_as_f64(q[row:row + 1, h]), _as_f64(k[k0:k1, h]), _as_f64(v[k0:k1, h]),
+                                  _as_f64(dout[row:row + 1, h]), float(scale), causal,
+                                  [row - cu_q[i]], cu_q[i + 1] - cu_q[i])
+        dqs.append(a[0])
+    dks, dvs = [], []
+    cache = {}
+    for row, h in k_samples:
+        i = owner(cu_k, row)
+        if (i, h) not in cache:
+            q0, q1 = cu_q[i], cu_q[i + 1]
+            k0, k1 = cu_k[i], cu_k[i + 1]
+            _, b, c = _attend_one_bwd(_as_f64(q[q0:q1, h]), _as_f64(k[k0:k1, h]), _as_f64(v[k0:k1, h]),
+                                      _as_f64(dout[q0:q1, h]), float(scale), causal,
+                                      list(range(q1 - q0)), q1 - q0)
+            cache[(i, h)] = (b, c)
+        b, c = cache[(i, h)]
+        dks.append(b[row - cu_k[i]])
+        dvs.append(c[row - cu_k[i]])
+    d = q.shape[2]
+    return (np.asarray(dqs).reshape(-1, d), np.asarray(dks).reshape(-1, d),
+            np.asarray(dvs).reshape(-1, d))

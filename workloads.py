@@ -33,6 +33,9 @@ Q, K and V are drawn together as float32 standard normals of shape
 ``[T, H, D]`` in the order q, k, v, scaled (workload 5 only), then rounded to
 the workload dtype with round-to-nearest-even (``torch.Tensor.to``).  Both the
 oracle and the GPU consume the rounded values.
+
+For gradient checks, the output gradient dO ``[T, H, D]`` is a separate
+float32 standard-normal draw with seed ``3000 + k``, rounded the same way.
 """
 
 from __future__ import annotations
@@ -45,6 +48,7 @@ import torch
 
 LENGTH_SEED_BASE = 1000
 VALUE_SEED_BASE = 2000
+GRAD_SEED_BASE = 3000
 
 DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 
@@ -160,6 +164,13 @@ def random_qkv(total_tokens: int, heads: int, head_dim: int, dtype: str,
             a *= np.float32(std)
         tensors.append(torch.from_numpy(a).to(DTYPES[dtype]))
     return tuple(tensors)
+
+
+def random_dout(total_tokens: int, heads: int, head_dim: int, dtype: str, seed: int):
+    """Draw an output gradient dO [T,H,D] as float32 N(0, 1), rounded to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((total_tokens, heads, head_dim), dtype=np.float32)
+    return torch.from_numpy(a).to(DTYPES[dtype])
 
 
 def make_workload(index: int, with_values: bool = True,
