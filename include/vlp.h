@@ -1,6 +1,6 @@
 /*
- * vlp.h -- packed variable-length attention forward for AMD Instinct MI355X
- * (gfx950): the C ABI of libvlp.so.
+ * vlp.h -- packed variable-length attention (forward and gradients) for AMD
+ * Instinct MI355X (gfx950): the C ABI of libvlp.so.
  *
  * The operation: a batch of B sequences is packed token-major into one buffer
  * [num_tokens, heads, head_dim]; sequence i occupies rows
@@ -252,6 +252,61 @@ vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k,
                                     const int32_t* grid_mapping, const int32_t* block_offsets,
                                     const int32_t* tile_order, int64_t num_blocks, int32_t block_m,
                                     void* stream);
+
+/*
+ * vlp_varlen_attn_bwd_workspace_size -- bytes of device workspace that
+ * vlp_varlen_attn_bwd needs: two fp32 [heads, rows_q] row statistics plus a
+ * device-built grid over the query lengths and one over the key lengths
+ * (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k, num_seqs, block_m)
+ * tiles), block_m = vlp_kernel_block_m(dtype, head_dim, causal, 0, ...).
+ * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, total_k < 0,
+ * heads < 1, block_m < 1 -> VLP_ERR_INVALID; rows beyond int32 ->
+ * VLP_ERR_OVERFLOW.
+ */
+vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                              int32_t block_m, size_t* bytes);
+
+/*
+ * vlp_varlen_attn_bwd -- gradients of vlp_varlen_attn_fwd with respect to q,
+ * k and v, given the output gradient dout.
+ *
+ * "gigl.nn.packed_attention", "Why this exists" (the packed attention is
+ * trained through; a backward kernel supplies its gradients) and "So you
+ * wanna CUDA Graph", "Correctness tangent" (gradients of inactive rows may
+ * stay undefined).  The pages give no backward algorithm; what is computed is
+ * the derivative of the forward: per sequence and head, with P its softmax
+ * weights, dv = P^T dout, dS = P * (dout v^T - rowsum(dout * out)),
+ * dq = scale * dS k, dk = scale * dS^T q.  Enqueues on `stream` two device
+ * grid builds and two kernels (dq over query tiles, then dk/dv over key
+ * tiles); no atomics, so the result is bitwise reproducible.
+ *
+ *   dtype          VLP_FP16 or VLP_BF16 (VLP_FP32 -> VLP_ERR_UNSUPPORTED);
+ *                  fp32 accumulation, gradients rounded to dtype.
+ *   q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
+ *   head_dim, max_seqlen, scale, causal   as for vlp_varlen_attn_fwd (no
+ *                  first-token mode).
+ *   out            device [rows_q, heads, head_dim], the forward's output.
+ *   dout           device [rows_q, heads, head_dim], gradient of the output.
+ *   lse            device fp32 [heads, rows_q], the forward's log-sum-exp.
+ *   dq             device [rows_q, heads, head_dim]: rows owned by a sequence
+ *                  are written (zeros for a query that sees no key); other
+ *                  rows are never written.
+ *   dk, dv         device [total_k, heads, head_dim]: rows owned by a
+ *                  sequence are written (zeros for a key that no query sees);
+ *                  other rows are never written.
+ *   workspace      device, >= vlp_varlen_attn_bwd_workspace_size bytes,
+ *                  256-byte aligned; overwritten.
+ * q, k, v, out, dout, dq, dk and dv must be 16-byte aligned, lse 4-byte.
+ * Errors: as vlp_varlen_attn_fwd, plus NULL dout/lse/dq/dk/dv/workspace ->
+ * VLP_ERR_NULL, misaligned dout/dq/dk/dv/lse/workspace -> VLP_ERR_INVALID,
+ * small workspace -> VLP_ERR_CAPACITY.
+ */
+vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                               int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* vlp_status_string -- a static, human-readable name for a status code; for
  * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */

@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for must in ("vlp_pack_sequences", "vlp_build_ragged_grid", "vlp_varlen_attn_fwd",
                  "vlp_varlen_attn_fwd_grid", "vlp_build_ragged_grid_device", "vlp_grid_capacity",
-                 "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string"):
+                 "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string",
+                 "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size"):
         assert must in names
 
 
@@ -249,6 +250,53 @@ def test_grid_forward_validation_errors():
     assert call(nb=-1) == 2
     assert call(bm=64) == 2                      # must equal vlp_kernel_block_m
     assert call(nb=2**31) == 5
+
+
+def _bwd(**kw):
+    lib = _lib.load()
+    a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100,
+             total_k=100, heads=2, head_dim=64, max_seqlen=0, scale=0.125, causal=0, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.vlp_varlen_attn_bwd(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["cu_q"],
+                                   a["cu_k"], a["b"], a["rows_q"], a["total_k"], a["heads"], a["head_dim"],
+                                   a["max_seqlen"], a["scale"], a["causal"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+def test_backward_validation_errors():
+    for name in ("q", "k", "v", "out", "dout", "lse", "cu_q", "cu_k", "dq", "dk", "dv", "ws"):
+        assert _bwd(**{name: None}) == 1, name
+    assert _bwd(dtype=0) == 3                   # fp32 gradients are not built
+    assert _bwd(dtype=7) == 3
+    assert _bwd(head_dim=48) == 3
+    assert _bwd(b=0) == 2
+    assert _bwd(heads=0) == 2
+    assert _bwd(total_k=-1) == 2
+    assert _bwd(scale=float("nan")) == 2
+    assert _bwd(scale=-1.0) == 2
+    assert _bwd(causal=3) == 2
+    for name in ("dout", "dq", "dk", "dv"):
+        assert _bwd(**{name: FAKE + 8}) == 2, name
+    assert _bwd(lse=FAKE + 2) == 2
+    assert _bwd(ws=FAKE + 64) == 2
+    assert _bwd(rows_q=2**31) == 5
+    assert _bwd(total_k=2**30, heads=4) == 5
+    assert _bwd(ws_bytes=64) == 4
+
+
+def test_backward_workspace_size():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.vlp_varlen_attn_bwd_workspace_size(64, 65536, 65536, 16, 128, None) == 1
+    assert lib.vlp_varlen_attn_bwd_workspace_size(0, 10, 10, 1, 128, ctypes.addressof(n)) == 2
+    assert lib.vlp_varlen_attn_bwd_workspace_size(4, 10, 10, 0, 128, ctypes.addressof(n)) == 2
+    assert lib.vlp_varlen_attn_bwd_workspace_size(4, 10, 10, 1, 0, ctypes.addressof(n)) == 2
+    assert lib.vlp_varlen_attn_bwd_workspace_size(64, 65536, 70000, 16, 128, ctypes.addressof(n)) == 0
+    cq = vlp.grid_capacity(65536, 64, 128)
+    ck = vlp.grid_capacity(70000, 64, 128)
+    assert n.value >= 2 * 4 * 16 * 65536 + 4 * (2 * 65 + 2 * cq + 2 * ck)
+    assert n.value == vlp.bwd_workspace_size(64, 65536, 70000, 16, 128)
 
 
 def test_device_grid_validation_errors():

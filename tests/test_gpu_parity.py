@@ -270,6 +270,21 @@ def test_zero_length_tail_and_nan_poisoned_capacity():
         assert torch.isnan(out[t:].float()).all().item() and torch.isnan(lse[:, t:]).all().item()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_scale_gives_uniform_weights(dtype):
+    """scale = 0: every visible key weighs the same, also where masking (a
+    ragged edge, the causal triangle) cuts a block."""
+    wl = workloads.custom_workload([1, 70, 129, 5], 2, 64, dtype, True, seed=15)
+    q, k, v, cu_d, cu_h = _to_dev(wl)
+    for causal in (False, True):
+        out, lse = vlp.varlen_attn_fwd(q, k, v, cu_d, cu_d, 0, 0.0, causal)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.varlen_attention(wl.q, wl.k, wl.v, cu_h.numpy(), cu_h.numpy(), 0.0, causal)
+        assert torch.isfinite(out.float()).all().item()
+        assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= TOL_OUT[dtype]
+        assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= TOL_LSE
+
+
 def test_causal_with_longer_keys():
     """Lq != Lk (cross-attention shapes): bottom-right causal alignment."""
     rng = np.random.default_rng(14)

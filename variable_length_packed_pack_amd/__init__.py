@@ -13,6 +13,9 @@ Functions mirror the pages' calls:
 * ``varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen, scale,
   causal, query_is_first_token, out, lse) -> (out, lse)``
   ("gigl.nn.packed_attention", packed_attention).
+* ``varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k,
+  max_seqlen, scale, causal) -> (dq, dk, dv)``, the gradients of the same
+  attention ("gigl.nn.packed_attention", "Why this exists").
 """
 
 from __future__ import annotations
@@ -210,3 +213,65 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()), stream)
     _lib.check(st, "varlen_attn_fwd")
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# attention gradients
+# ---------------------------------------------------------------------------
+
+def bwd_workspace_size(num_seqs: int, rows_q: int, total_k: int, heads: int, block_m: int) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().vlp_varlen_attn_bwd_workspace_size(int(num_seqs), int(rows_q), int(total_k), int(heads),
+                                                              int(block_m), ctypes.addressof(n)),
+               "bwd_workspace_size")
+    return int(n.value)
+
+
+def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                    lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                    max_seqlen: int = 0, scale: Optional[float] = None, causal: bool = False,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None, *, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of ``varlen_attn_fwd`` on the current stream.
+
+    ``out`` and ``lse`` are the forward's results for the same arguments;
+    ``dout`` has the shape of ``out``.  Rows owned by no sequence are never
+    written (fresh outputs are allocated with ``torch.empty``).
+    """
+    lib = _lib.load()
+    tensors = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k)
+    if not all(t.is_cuda for t in tensors):
+        raise ValueError("all inputs must be device tensors")
+    if q.dtype not in _DTYPE_CODES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise TypeError("q, k, v, out, dout must share one of float32 / float16 / bfloat16")
+    if q.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:] or out.shape != q.shape \
+            or dout.shape != q.shape:
+        raise ValueError("q/out/dout [rows, H, D] and k, v [T, H, D] with matching H, D")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]):
+        raise ValueError("lse must be float32 [H, rows]")
+    for t in (q, k, v, out, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    rows_q, heads, head_dim = (int(x) for x in q.shape)
+    total_k = int(k.shape[0])
+    b = int(cu_seqlens_k.numel()) - 1
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    code = _DTYPE_CODES[q.dtype]
+    if workspace is None:
+        bm = lib.vlp_kernel_block_m(code, head_dim, int(bool(causal)), 0, b, rows_q, int(max_seqlen))
+        if bm < 1:
+            raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_bwd")
+        nbytes = bwd_workspace_size(b, rows_q, total_k, heads, bm)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    st = lib.vlp_varlen_attn_bwd(code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim,
+                                 int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), int(workspace.numel()), _stream_handle(q.device))
+    _lib.check(st, "varlen_attn_bwd")
+    return dq, dk, dv

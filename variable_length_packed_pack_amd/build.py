@@ -41,6 +41,8 @@ SOURCES = [
     "attn_bf16.hip",
     "attn_f16.hip",
     "attn_f32.hip",
+    "attn_bwd_bf16.hip",
+    "attn_bwd_f16.hip",
 ]
 
 

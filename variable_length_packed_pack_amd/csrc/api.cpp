@@ -69,6 +69,12 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
   return VLP_OK;
 }
 
+// Factor taking raw scores to exp2 units.  Masked scores are -inf and must
+// map to -inf, which -inf * 0 would not: a zero scale is replaced by the
+// smallest normal float, which leaves every finite score at (nearly) 0, so
+// exp2 returns exactly 1 and the weights are exactly uniform, as for scale 0.
+float exp2_factor(float scale) { return scale > 0.0f ? scale * 1.4426950408889634f : 1.17549435e-38f; }
+
 vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
                         int32_t num_seqs, int64_t rows_q, int32_t heads, float scale, void* out, float* lse) {
   vlp::AttnArgs a{};
@@ -83,7 +89,7 @@ vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32
   a.heads = heads;
   a.rows_q = static_cast<int32_t>(rows_q);
   a.num_blocks = -1;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = exp2_factor(scale);
   return a;
 }
 
@@ -98,6 +104,40 @@ vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int3
     case VLP_FP16: return hip_status(vlp::launch_attn_f16(a, head_dim, causal != 0, blocks, s));
     default: return hip_status(vlp::launch_attn_f32(a, head_dim, causal != 0, blocks, s));
   }
+}
+
+// Workspace of the backward: [lse2 | delta | query grid | key grid], each
+// 256-byte aligned; lse2 and delta are fp32 [heads, rows_q].
+struct BwdWorkspace {
+  size_t off_lse2, off_delta, off_qgrid, off_kgrid, bytes;
+  int64_t cap_q, cap_k;
+  GridWorkspace qg, kg;
+};
+
+BwdWorkspace bwd_workspace(int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads, int32_t block) {
+  BwdWorkspace w;
+  const size_t stats = round_up(sizeof(float) * static_cast<size_t>(heads) * static_cast<size_t>(rows_q), 256);
+  w.cap_q = vlp_grid_capacity(rows_q, num_seqs, block);
+  w.cap_k = vlp_grid_capacity(total_k, num_seqs, block);
+  w.qg = grid_workspace(num_seqs, w.cap_q);
+  w.kg = grid_workspace(num_seqs, w.cap_k);
+  w.off_lse2 = 0;
+  w.off_delta = stats;
+  w.off_qgrid = 2 * stats;
+  w.off_kgrid = w.off_qgrid + w.qg.bytes;
+  w.bytes = w.off_kgrid + w.kg.bytes;
+  return w;
+}
+
+vlp_status launch_bwd(int32_t dtype, bool dkdv, const vlp::BwdArgs& a, int32_t head_dim, bool causal,
+                      int64_t blocks, hipStream_t s) {
+  if (blocks <= 0) return VLP_OK;
+  if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
+  if (dtype == VLP_BF16)
+    return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_bf16(a, head_dim, causal, blocks, s)
+                           : vlp::launch_attn_bwd_dq_bf16(a, head_dim, causal, blocks, s));
+  return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f16(a, head_dim, causal, blocks, s)
+                         : vlp::launch_attn_bwd_dq_f16(a, head_dim, causal, blocks, s));
 }
 
 }  // namespace
@@ -203,4 +243,88 @@ extern "C" const char* vlp_status_string(vlp_status status) {
     case VLP_ERR_HIP: return g_hip_error;
     default: return "unknown vlp status";
   }
+}
+
+extern "C" vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                                         int32_t heads, int32_t block_m, size_t* bytes) {
+  if (!bytes) return VLP_ERR_NULL;
+  if (num_seqs < 1 || rows_q < 0 || total_k < 0 || heads < 1 || block_m < 1) return VLP_ERR_INVALID;
+  if (rows_q > INT32_MAX || total_k > INT32_MAX) return VLP_ERR_OVERFLOW;
+  *bytes = bwd_workspace(num_seqs, rows_q, total_k, heads, block_m).bytes;
+  return VLP_OK;
+}
+
+extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const void* out, const void* dout, const float* lse,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                          int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  Checked c{};
+  vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
+                                head_dim, max_seqlen, scale, causal, 0, out, &c);
+  if (st != VLP_OK) return st;
+  if (!dout || !lse || !dq || !dk || !dv || !workspace) return VLP_ERR_NULL;
+  if (dtype == VLP_FP32) return VLP_ERR_UNSUPPORTED;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return VLP_ERR_INVALID;
+  if (rows_q * heads > INT32_MAX || total_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  const BwdWorkspace w = bwd_workspace(num_seqs, rows_q, total_k, heads, c.block_m);
+  if (w.cap_q * heads > INT32_MAX || w.cap_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  if (workspace_bytes < w.bytes) return VLP_ERR_CAPACITY;
+
+  char* base = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  vlp::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.lse2 = reinterpret_cast<float*>(base + w.off_lse2);
+  a.delta = reinterpret_cast<float*>(base + w.off_delta);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.num_seqs = num_seqs;
+  a.heads = heads;
+  a.rows_q = static_cast<int32_t>(rows_q);
+  a.scale = scale;
+  a.scale_log2 = exp2_factor(scale);
+
+  // dQ over the query grid first: it also writes lse2 and delta, which the
+  // dK/dV launch (same stream) reads.
+  if (w.cap_q > 0) {
+    char* g = base + w.off_qgrid;
+    int32_t* bo = reinterpret_cast<int32_t*>(g + w.qg.off_bo);
+    int32_t* gm = reinterpret_cast<int32_t*>(g + w.qg.off_gm);
+    int32_t* to = reinterpret_cast<int32_t*>(g + w.qg.off_to);
+    st = hip_status(vlp::launch_grid_build(cu_seqlens_q, num_seqs, c.block_m, bo, gm, to, w.cap_q, s));
+    if (st != VLP_OK) return st;
+    a.grid_mapping = gm;
+    a.block_offsets = bo;
+    a.tile_order = to;
+    a.grid_cap = static_cast<int32_t>(w.cap_q);
+    st = launch_bwd(dtype, false, a, head_dim, causal != 0, w.cap_q * heads, s);
+    if (st != VLP_OK) return st;
+  }
+  if (w.cap_k > 0) {
+    char* g = base + w.off_kgrid;
+    int32_t* bo = reinterpret_cast<int32_t*>(g + w.kg.off_bo);
+    int32_t* gm = reinterpret_cast<int32_t*>(g + w.kg.off_gm);
+    int32_t* to = reinterpret_cast<int32_t*>(g + w.kg.off_to);
+    st = hip_status(vlp::launch_grid_build(cu_seqlens_k, num_seqs, c.block_m, bo, gm, to, w.cap_k, s));
+    if (st != VLP_OK) return st;
+    a.grid_mapping = gm;
+    a.block_offsets = bo;
+    a.tile_order = to;
+    a.grid_cap = static_cast<int32_t>(w.cap_k);
+    st = launch_bwd(dtype, true, a, head_dim, causal != 0, w.cap_k * heads, s);
+  }
+  return st;
 }

@@ -1,0 +1,14 @@
+// Tiled packed-attention backward, bf16 inputs: template instances.
+#include "attn_bwd_launch.h"
+
+namespace vlp {
+
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s) {
+  return bwd_launch<VLP_BF16, false>(a, head_dim, causal, blocks, s);
+}
+
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s) {
+  return bwd_launch<VLP_BF16, true>(a, head_dim, causal, blocks, s);
+}
+
+}  // namespace vlp

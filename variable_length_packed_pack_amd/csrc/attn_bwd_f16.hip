@@ -1,0 +1,14 @@
+// Tiled packed-attention backward, fp16 inputs: template instances.
+#include "attn_bwd_launch.h"
+
+namespace vlp {
+
+hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s) {
+  return bwd_launch<VLP_FP16, false>(a, head_dim, causal, blocks, s);
+}
+
+hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s) {
+  return bwd_launch<VLP_FP16, true>(a, head_dim, causal, blocks, s);
+}
+
+}  // namespace vlp

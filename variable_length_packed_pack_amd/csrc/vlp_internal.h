@@ -33,6 +33,33 @@ struct AttnArgs {
   float scale_log2;            // scale * log2(e): scores go straight to exp2
 };
 
+// Arguments of the two backward launches (the dQ kernel over the query
+// grid, the dK/dV kernel over the key grid), passed by value.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;            // [heads, rows_q], from the forward
+  float* lse2;                 // [heads, rows_q] workspace: lse * log2(e), +inf for keyless rows
+  float* delta;                // [heads, rows_q] workspace: rowsum(dout * out)
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* cu_q;         // [num_seqs + 1]
+  const int32_t* cu_k;         // [num_seqs + 1]
+  const int32_t* grid_mapping; // grid of this launch (query grid or key grid)
+  const int32_t* block_offsets;
+  const int32_t* tile_order;
+  int32_t num_seqs;
+  int32_t heads;
+  int32_t rows_q;
+  int32_t grid_cap;
+  float scale;                 // factor of dq and dk
+  float scale_log2;            // scores -> exp2 units
+};
+
 // Kernel families and their tile shapes.  block_m is the query rows per
 // workgroup tile; it is what the ragged grid is built with.
 struct TileShape {
@@ -53,6 +80,12 @@ hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t
 // First-token forward: one wavefront per (sequence, head), `slots` sequences.
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
                                    int64_t slots, hipStream_t s);
+
+// Backward launches (16-bit element types), `blocks` workgroups each.
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 
 // Device ragged-grid build (one workgroup).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
