@@ -7,6 +7,9 @@
 
 namespace vlp {
 
+// Query rows per streamed block of the dK/dV kernel.
+constexpr int kBwdBlockQ = 64;
+
 template <int DT, int D, bool CAUSAL>
 hipError_t bwd_dq_go(const BwdArgs& a, int64_t blocks, hipStream_t s) {
   constexpr int NW = tile_waves(DT, D);

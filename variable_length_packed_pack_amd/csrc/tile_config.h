@@ -11,8 +11,6 @@ constexpr int tile_waves(int dtype, int head_dim) {
   return dtype == VLP_FP32 ? 2 : (head_dim == 128 ? 4 : 2);
 }
 constexpr int tile_block_n(int dtype, int /*head_dim*/) { return dtype == VLP_FP32 ? 32 : 64; }
-// Query rows per streamed block of the dK/dV backward kernel.
-constexpr int kBwdBlockQ = 64;
 constexpr bool head_dim_built(int head_dim) {
   return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
 }
