@@ -280,8 +280,8 @@ vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, 
  * grid builds and two kernels (dq over query tiles, then dk/dv over key
  * tiles); no atomics, so the result is bitwise reproducible.
  *
- *   dtype          VLP_FP16 or VLP_BF16 (VLP_FP32 -> VLP_ERR_UNSUPPORTED);
- *                  fp32 accumulation, gradients rounded to dtype.
+ *   dtype          VLP_FP32, VLP_FP16 or VLP_BF16; fp32 accumulation,
+ *                  gradients rounded to dtype.
  *   q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
  *   head_dim, max_seqlen, scale, causal   as for vlp_varlen_attn_fwd (no
  *                  first-token mode).

@@ -267,7 +267,6 @@ def _bwd(**kw):
 def test_backward_validation_errors():
     for name in ("q", "k", "v", "out", "dout", "lse", "cu_q", "cu_k", "dq", "dk", "dv", "ws"):
         assert _bwd(**{name: None}) == 1, name
-    assert _bwd(dtype=0) == 3                   # fp32 gradients are not built
     assert _bwd(dtype=7) == 3
     assert _bwd(head_dim=48) == 3
     assert _bwd(b=0) == 2

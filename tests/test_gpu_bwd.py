@@ -20,7 +20,10 @@ Tolerance (derived; the pages give none for gradients), per gradient row
     which moves it by about 2^-9 * sqrt(D) * |dO| |O| (measured: smaller
     than the dS term).
 Together these stay below 2^-7 of the row's largest element; 2e-2 absolute
-covers rows of small gradients, as for the forward's output.
+covers rows of small gradients, as for the forward's output.  fp32 inputs
+keep every operand in fp32 (fp32 matrix cores): 1e-4 absolute, as for the
+forward's output, plus 2^-14 of the row's largest element for the
+accumulation over long rows.
 """
 
 import sys
@@ -36,8 +39,8 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-ATOL = {"fp16": 2e-2, "bf16": 2e-2}
-RTOL = {"fp16": 2.0 ** -7, "bf16": 2.0 ** -7}
+ATOL = {"fp32": 1e-4, "fp16": 2e-2, "bf16": 2e-2}
+RTOL = {"fp32": 2.0 ** -14, "fp16": 2.0 ** -7, "bf16": 2.0 ** -7}
 
 
 def _say(msg):
@@ -101,7 +104,8 @@ def _workload_with_grad(k, dtype):
 # whole workloads, every row
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("k,dtype", [(1, "bf16"), (2, "bf16"), (2, "fp16"), (3, "bf16"), (3, "fp16")])
+@pytest.mark.parametrize("k,dtype", [(1, "fp32"), (1, "bf16"), (2, "fp32"), (2, "bf16"), (2, "fp16"), (3, "bf16"),
+                                     (3, "fp16"), (3, "fp32")])
 def test_bwd_workload_every_row(k, dtype):
     wl, dout = _workload_with_grad(k, dtype)
     cu = torch.from_numpy(wl.cu_seqlens_host())
@@ -113,7 +117,7 @@ def test_bwd_workload_every_row(k, dtype):
 # edge cases
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("head_dim", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_every_head_dim(dtype, head_dim, causal):
@@ -143,7 +147,7 @@ def test_bwd_cross_lengths_keyless_queries_and_unowned_rows():
     h, d = 2, 128
     cap_q, cap_k = sum(lq) + 11, sum(lk) + 13
     cq, ck = _cu(lq), _cu(lk)
-    for dtype in ("bf16", "fp16"):
+    for dtype in ("bf16", "fp16", "fp32"):
         tdt = workloads.DTYPES[dtype]
 
         def draw(rows, total):

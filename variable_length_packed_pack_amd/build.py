@@ -43,6 +43,7 @@ SOURCES = [
     "attn_f32.hip",
     "attn_bwd_bf16.hip",
     "attn_bwd_f16.hip",
+    "attn_bwd_f32.hip",
 ]
 
 

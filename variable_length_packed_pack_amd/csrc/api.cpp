@@ -133,11 +133,17 @@ vlp_status launch_bwd(int32_t dtype, bool dkdv, const vlp::BwdArgs& a, int32_t h
                       int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return VLP_OK;
   if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
-  if (dtype == VLP_BF16)
-    return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_bf16(a, head_dim, causal, blocks, s)
-                           : vlp::launch_attn_bwd_dq_bf16(a, head_dim, causal, blocks, s));
-  return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f16(a, head_dim, causal, blocks, s)
-                         : vlp::launch_attn_bwd_dq_f16(a, head_dim, causal, blocks, s));
+  switch (dtype) {
+    case VLP_BF16:
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_bf16(a, head_dim, causal, blocks, s)
+                             : vlp::launch_attn_bwd_dq_bf16(a, head_dim, causal, blocks, s));
+    case VLP_FP16:
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f16(a, head_dim, causal, blocks, s)
+                             : vlp::launch_attn_bwd_dq_f16(a, head_dim, causal, blocks, s));
+    default:
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f32(a, head_dim, causal, blocks, s)
+                             : vlp::launch_attn_bwd_dq_f32(a, head_dim, causal, blocks, s));
+  }
 }
 
 }  // namespace
@@ -266,7 +272,6 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
                                 head_dim, max_seqlen, scale, causal, 0, out, &c);
   if (st != VLP_OK) return st;
   if (!dout || !lse || !dq || !dk || !dv || !workspace) return VLP_ERR_NULL;
-  if (dtype == VLP_FP32) return VLP_ERR_UNSUPPORTED;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return VLP_ERR_INVALID;

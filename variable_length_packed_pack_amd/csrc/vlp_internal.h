@@ -81,11 +81,13 @@ hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
                                    int64_t slots, hipStream_t s);
 
-// Backward launches (16-bit element types), `blocks` workgroups each.
+// Backward launches, `blocks` workgroups each.
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 
 // Device ragged-grid build (one workgroup).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
