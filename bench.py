@@ -19,6 +19,13 @@ Also measured in the same run:
 
 Prints ONE JSON line.  Default workload: the Zipf decoder batch (64 sequences,
 Zipf s = 1 over 65,536 tokens, 16 heads x 128, causal, bf16).
+
+``--backward`` measures the gradients instead: one step = pack_sequences, the
+cu_seqlens copy, two device grid builds, the dq kernel and the dk/dv kernel,
+with q, k, v, out, lse and dout resident; the rate counts 2.5x the forward's
+algorithmic flops (the five products S, dP, dV, dK, dQ), the roofline is that
+of the dk/dv kernel (its four products, 2x the forward's flops), and the
+padded comparator is torch SDPA's backward over the padded envelope.
 """
 
 from __future__ import annotations
@@ -43,16 +50,20 @@ METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 
 # Sources of the 16-bit tiled attention kernel (the roofline kernel of the
 # bench line); a committed HBM-traffic profile is used only while they match.
 KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_bf16.hip", "tile_config.h"]
+METRIC_BWD = "varlen attn bwd TFLOP/s (2.5x forward real-token flops; % MFMA peak) + speedup vs padded, 1 GPU"
+# Sources of the 16-bit dk/dv kernel (the roofline kernel of the backward line).
+KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_bf16.hip", "attn_fwd_mfma.h",
+                      "tile_config.h"]
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "variable_length_packed_pack_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -75,10 +86,10 @@ def compulsory_bytes(rows_q: int, total_k: int, heads: int, head_dim: int, elt: 
     return (2.0 * rows_q + 2.0 * total_k) * heads * head_dim * elt + 4.0 * rows_q * heads
 
 
-def traffic_from_profile(workload: str, src_hash: str):
+def traffic_from_profile(workload: str, src_hash: str, kernel: str = "attn_fwd"):
     """HBM bytes per launch from a committed rocprofv3 PMC summary, or None
     when no summary matches the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -191,6 +202,213 @@ def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
     return total_ms, backend_used
 
 
+def cpu_oracle_baseline_bwd(wl, dout, budget_s: float):
+    """The oracle's gradients on whole heads of the same batch until the
+    budget is spent (at least one head); rate in 2.5x forward flops."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    cu = wl.cu_seqlens_host()
+    elapsed, heads_done = 0.0, 0
+    while heads_done < wl.heads and (heads_done == 0 or elapsed < budget_s):
+        hh = heads_done
+        sl = slice(hh, hh + 1)
+        q, k, v = (x[:, sl].float().numpy() for x in (wl.q, wl.k, wl.v))
+        g = dout[:, sl].float().numpy()
+        t0 = time.perf_counter()
+        oracle.varlen_attention_bwd(q, k, v, g, cu, cu, wl.scale, wl.causal)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+    flops = 2.5 * algorithmic_flops(wl.lengths, heads_done, wl.head_dim, wl.causal)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"gradients of {heads_done} of {wl.heads} heads, all {wl.num_seqs} sequences "
+                   f"({flops / 1e9:.1f} GFLOP at 2.5x forward), fp64 numpy, {elapsed:.1f} s"),
+        "seconds": elapsed,
+    }
+
+
+def padded_backward_comparator(wl, q, k, v, dout, reps: int):
+    """torch SDPA's backward over the padded envelope (forward outside the
+    timed region), chunked over the batch; returns (ms, backend)."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    b, h, d = wl.num_seqs, wl.heads, wl.head_dim
+    lmax = wl.max_len
+    cu = wl.cu_seqlens_host()
+    per_seq = 10 * h * lmax * d * q.element_size()
+    chunk = max(1, min(b, int(40e9 // per_seq)))
+    total_ms, backend_used = 0.0, None
+    for c0 in range(0, b, chunk):
+        c1 = min(b, c0 + chunk)
+        nb = c1 - c0
+        pads = [torch.zeros(nb, h, lmax, d, dtype=q.dtype, device=q.device) for _ in range(4)]
+        for j, i in enumerate(range(c0, c1)):
+            s0, e0 = int(cu[i]), int(cu[i + 1])
+            for src, dst in zip((q, k, v, dout), pads):
+                dst[j, :, : e0 - s0] = src[s0:e0].transpose(0, 1)
+        qp, kp, vp, dop = pads
+        for t in (qp, kp, vp):
+            t.requires_grad_(True)
+        mask = None
+        if not wl.causal:
+            lens = torch.as_tensor(wl.lengths[c0:c1], device=q.device)
+            mask = (torch.arange(lmax, device=q.device)[None, :] < lens[:, None])[:, None, None, :]
+        ran, out = None, None
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            if mask is not None and be == SDPBackend.FLASH_ATTENTION:
+                continue
+            try:
+                with sdpa_kernel([be]):
+                    out = torch.nn.functional.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask,
+                                                                           is_causal=wl.causal, scale=wl.scale)
+                    torch.autograd.grad(out, (qp, kp, vp), dop, retain_graph=True)
+                torch.cuda.synchronize()
+                ran = be
+                break
+            except RuntimeError:
+                out = None
+                continue
+        if ran is None:
+            return None, "none (no fused SDPA backend accepted the envelope)"
+        backend_used = str(ran).split(".")[-1]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            torch.autograd.grad(out, (qp, kp, vp), dop, retain_graph=True)
+        end.record()
+        torch.cuda.synchronize()
+        total_ms += start.elapsed_time(end) / reps
+        del qp, kp, vp, dop, out, pads
+        torch.cuda.empty_cache()
+    return total_ms, backend_used
+
+
+def bench_backward(args, wl, dev) -> int:
+    """The gradient step; see the module docstring."""
+    import torch
+
+    import variable_length_packed_pack_amd as vlp
+    import workloads
+
+    k_idx = workloads.WORKLOAD_NAMES[args.workload]
+    t, h, d, b = wl.total_tokens, wl.heads, wl.head_dim, wl.num_seqs
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    dout_host = workloads.random_dout(t, h, d, wl.dtype, workloads.GRAD_SEED_BASE + k_idx)
+    dout = dout_host.to(dev)
+    cu_host = torch.from_numpy(wl.cu_seqlens_host())
+    cu_dev = cu_host.to(dev)
+    out, lse = vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, False, b, t, wl.max_len)
+    ws = torch.empty(vlp.bwd_workspace_size(b, t, t, h, bm), dtype=torch.uint8, device=dev)
+    fwd_flops = algorithmic_flops(wl.lengths, h, d, wl.causal)
+    flops = 2.5 * fwd_flops
+    lengths_host = wl.lengths.copy()
+    n_steps = args.warmup + args.steps
+    pinned = [torch.empty(b + 1, dtype=torch.int32).pin_memory() for _ in range(n_steps)]
+    cu_step = torch.empty(b + 1, dtype=torch.int32, device=dev)
+
+    def step(i: int) -> None:
+        _, cu = vlp.pack_sequences(lengths_host, wl.max_len)
+        pinned[i].copy_(cu)
+        cu_step.copy_(pinned[i], non_blocking=True)
+        vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_step, cu_step, wl.max_len, wl.scale, wl.causal, dq, dk, dv,
+                            workspace=ws)
+
+    log(f"[bench] backward: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] backward: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # each kernel alone: cached grids, HIP events on the stream they run on
+    gh = vlp.build_ragged_grid(cu_host, bm)
+    grid = vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev), gh.tile_order.to(dev), gh.num_blocks, bm)
+    stats = torch.empty(2, h, t, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    reps = args.kernel_only_reps or args.steps
+    torch.cuda.synchronize()
+    kernel_ms = {}
+    with torch.cuda.stream(stream):
+        vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk, dv,
+                            grids=(grid, grid), row_stats=stats, phases=vlp.VLP_BWD_DQ | vlp.VLP_BWD_DKDV)
+        for name, ph in (("dkdv", vlp.VLP_BWD_DKDV), ("dq", vlp.VLP_BWD_DQ)):
+            for _ in range(2):
+                vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk,
+                                    dv, grids=(grid, grid), row_stats=stats, phases=ph)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk,
+                                    dv, grids=(grid, grid), row_stats=stats, phases=ph)
+            ev1.record(stream)
+            stream.synchronize()
+            kernel_ms[name] = ev0.elapsed_time(ev1) / reps
+    torch.cuda.synchronize()
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    dkdv_flops = 2.0 * fwd_flops
+    roof = {"bound": "mfma", "achieved": round(dkdv_flops / (kernel_ms["dkdv"] * 1e-3) / 1e12, 3),
+            "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    src_hash = kernel_source_hash(KERNEL_SOURCES_BWD)
+    traffic = traffic_from_profile(args.workload, src_hash, kernel="attn_bwd_dkdv")
+    log(f"[bench] backward step {ms_per_step:.3f} ms  dkdv {kernel_ms['dkdv']:.3f} ms  dq {kernel_ms['dq']:.3f} ms")
+
+    padded_ms, padded_backend = (None, "skipped")
+    if not args.no_padded:
+        log("[bench] padded SDPA backward comparator")
+        padded_ms, padded_backend = padded_backward_comparator(wl, q, k, v, dout, reps=3)
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline (gradients)")
+        cpu = cpu_oracle_baseline_bwd(wl, dout_host, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC_BWD,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; no dataset)",
+        "config": {"workload": wl.name, "pass": "backward", "num_seqs": b, "total_tokens": t,
+                   "max_seqlen": wl.max_len, "heads": h, "head_dim": d, "causal": wl.causal, "block_m": bm},
+        "roofline": {**roof, "traffic": traffic},
+        "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
+        "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
+        "padded_ms": None if padded_ms is None else round(padded_ms, 3),
+        "padded_backend": padded_backend,
+        "kernel_ms": {kk: round(vv, 4) for kk, vv in kernel_ms.items()},
+        "dkdv_kernel_tflops": roof["achieved"],
+        "dq_kernel_tflops": round(1.5 * fwd_flops / (kernel_ms["dq"] * 1e-3) / 1e12, 3),
+        "kernel_source_hash": src_hash,
+        "algorithmic_gflop": round(flops / 1e9, 3),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +421,8 @@ def main() -> int:
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
     ap.add_argument("--first-token", action="store_true",
                     help="query_is_first_token mode: one query per sequence (its first token)")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the gradients (dq, dk, dv) instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
                          "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -235,6 +455,11 @@ def main() -> int:
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)
+    if args.backward:
+        if args.first_token:
+            print("--backward has no first-token mode", file=sys.stderr)
+            return 2
+        return bench_backward(args, wl, dev)
     ft = args.first_token
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
     t, h, d = wl.total_tokens, wl.heads, wl.head_dim

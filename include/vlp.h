@@ -308,6 +308,45 @@ vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, cons
                                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * vlp_varlen_attn_bwd_grid -- the same gradients with caller-supplied, cached
+ * tile metadata ("PyCoRa", "CoRa Metadata": computed once and cached) and a
+ * caller-owned row-statistics buffer, run in one or both phases.
+ *
+ *   q_grid_mapping, q_block_offsets, q_tile_order, q_num_blocks
+ *                  the ragged grid of cu_seqlens_q, as built by
+ *                  vlp_build_ragged_grid(_device) with block_m (tile_order
+ *                  may be NULL: natural order); q_num_blocks * heads
+ *                  workgroups run the dq phase.
+ *   k_grid_mapping, k_block_offsets, k_tile_order, k_num_blocks
+ *                  the same for cu_seqlens_k; they run the dk/dv phase.
+ *   block_m        must equal vlp_kernel_block_m(dtype, head_dim, causal, 0,
+ *                  ...); both grids use it.
+ *   row_stats      device fp32 [2, heads, rows_q], 4-byte aligned: written by
+ *                  the dq phase (the log-sum-exp in base-2 units and
+ *                  rowsum(dout * out) of every owned query row), read by the
+ *                  dk/dv phase.
+ *   phases         VLP_BWD_DQ, VLP_BWD_DKDV or both (dq first).  The dk/dv
+ *                  phase alone needs row_stats from an earlier dq phase on
+ *                  the same inputs.
+ * Errors: as vlp_varlen_attn_bwd (no workspace), plus NULL row_stats or a
+ * NULL grid of a requested phase -> VLP_ERR_NULL; phases outside 1..3, a
+ * block_m mismatch, negative block counts, misaligned row_stats ->
+ * VLP_ERR_INVALID; block counts * heads beyond int32 -> VLP_ERR_OVERFLOW.
+ */
+#define VLP_BWD_DQ 1
+#define VLP_BWD_DKDV 2
+vlp_status vlp_varlen_attn_bwd_grid(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
+                                    const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                    int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale,
+                                    int32_t causal, void* dq, void* dk, void* dv, const int32_t* q_grid_mapping,
+                                    const int32_t* q_block_offsets, const int32_t* q_tile_order,
+                                    int64_t q_num_blocks, const int32_t* k_grid_mapping,
+                                    const int32_t* k_block_offsets, const int32_t* k_tile_order,
+                                    int64_t k_num_blocks, int32_t block_m, float* row_stats, int32_t phases,
+                                    void* stream);
+
 /* vlp_status_string -- a static, human-readable name for a status code; for
  * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */
 const char* vlp_status_string(vlp_status status);

@@ -49,6 +49,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert f"#define VLP_DEVICE_SORT_MAX_SEQS {_lib.VLP_DEVICE_SORT_MAX_SEQS}" in text
     assert "#define VLP_FIRST_TOKEN_BLOCK_M (1 << 30)" in text
+    assert f"#define VLP_BWD_DQ {_lib.VLP_BWD_DQ}" in text and f"#define VLP_BWD_DKDV {_lib.VLP_BWD_DKDV}" in text
     for name in ("VLP_FP32 = 0", "VLP_FP16 = 1", "VLP_BF16 = 2", "VLP_OK = 0", "VLP_ERR_HIP = 6"):
         assert name in text
 
@@ -282,6 +283,31 @@ def test_backward_validation_errors():
     assert _bwd(rows_q=2**31) == 5
     assert _bwd(total_k=2**30, heads=4) == 5
     assert _bwd(ws_bytes=64) == 4
+
+
+def test_grid_backward_validation_errors():
+    lib = _lib.load()
+    bm = lib.vlp_kernel_block_m(2, 64, 0, 0, 4, 100, 0)
+
+    def call(**kw):
+        a = dict(qgm=FAKE, qbo=FAKE, qn=3, kgm=FAKE, kbo=FAKE, kn=3, bm=bm, stats=FAKE, phases=3, dq=FAKE)
+        a.update(kw)
+        return lib.vlp_varlen_attn_bwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, 64,
+                                            0, 0.1, 0, a["dq"], FAKE, FAKE, a["qgm"], a["qbo"], None, a["qn"],
+                                            a["kgm"], a["kbo"], None, a["kn"], a["bm"], a["stats"], a["phases"],
+                                            None)
+    assert call(dq=None) == 1
+    assert call(stats=None) == 1
+    assert call(qgm=None) == 1
+    assert call(kbo=None) == 1
+    assert call(qgm=None, phases=2) != 1        # the dq grid is not needed for the dk/dv phase alone
+    assert call(kgm=None, phases=1) != 1
+    assert call(phases=0) == 2
+    assert call(phases=4) == 2
+    assert call(bm=bm // 2) == 2
+    assert call(qn=-1) == 2
+    assert call(stats=FAKE + 2) == 2
+    assert call(kn=2**31) == 5
 
 
 def test_backward_workspace_size():

@@ -216,6 +216,34 @@ def test_bwd_bitwise_deterministic_and_sequence_independent():
         assert np.array_equal(x[keep], y[keep])
 
 
+def test_bwd_cached_grids_phases_and_tile_order_bitwise():
+    """The cached-grid entry point equals the workspace one bit for bit, run
+    as one call or as the dq phase then the dk/dv phase, with the longest-
+    first or the natural tile order."""
+    lengths = [300, 17, 0, 129, 1, 64, 200]
+    h, d = 4, 128
+    wl = workloads.custom_workload(lengths, h, d, "bf16", True, seed=24)
+    dout = workloads.random_dout(wl.total_tokens, h, d, "bf16", seed=25)
+    cu = _cu(lengths)
+    q, k, v, do = (t.to(DEV) for t in (wl.q, wl.k, wl.v, dout))
+    cud = cu.to(DEV)
+    out, lse = vlp.varlen_attn_fwd(q, k, v, cud, cud, 0, wl.scale, True)
+    ref = vlp.varlen_attn_bwd(q, k, v, out, do, lse, cud, cud, 0, wl.scale, True)
+    bm = vlp.kernel_block_m(q.dtype, d, True)
+    gh = vlp.build_ragged_grid(cu, bm)
+    g = vlp.RaggedGrid(gh.grid_mapping.to(DEV), gh.block_offsets.to(DEV), gh.tile_order.to(DEV), gh.num_blocks, bm)
+    natural = g._replace(tile_order=None)
+    for grids, phases in (((g, g), (3,)), ((g, g), (1, 2)), ((natural, natural), (3,))):
+        dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+        stats = torch.empty(2, h, q.shape[0], dtype=torch.float32, device=DEV)
+        for ph in phases:
+            vlp.varlen_attn_bwd(q, k, v, out, do, lse, cud, cud, 0, wl.scale, True, dq, dk, dv, grids=grids,
+                                row_stats=stats, phases=ph)
+        torch.cuda.synchronize()
+        for x, y in zip((dq, dk, dv), ref):
+            assert torch.equal(x, y)
+
+
 # --------------------------------------------------------------------------
 # the Zipf batch at full size, in the configuration the benchmark times
 # --------------------------------------------------------------------------

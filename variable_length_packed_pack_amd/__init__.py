@@ -30,6 +30,8 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     VLP_BF16,
+    VLP_BWD_DKDV,
+    VLP_BWD_DQ,
     VLP_DEVICE_SORT_MAX_SEQS,
     VLP_FIRST_TOKEN_BLOCK_M,
     VLP_FP16,
@@ -231,12 +233,19 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                     lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                     max_seqlen: int = 0, scale: Optional[float] = None, causal: bool = False,
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                    dv: Optional[torch.Tensor] = None, *, workspace: Optional[torch.Tensor] = None):
+                    dv: Optional[torch.Tensor] = None, *, workspace: Optional[torch.Tensor] = None,
+                    grids: Optional[tuple] = None, row_stats: Optional[torch.Tensor] = None,
+                    phases: int = 3):
     """Gradients (dq, dk, dv) of ``varlen_attn_fwd`` on the current stream.
 
     ``out`` and ``lse`` are the forward's results for the same arguments;
     ``dout`` has the shape of ``out``.  Rows owned by no sequence are never
     written (fresh outputs are allocated with ``torch.empty``).
+    ``grids``: cached device metadata ``(query_grid, key_grid)`` from
+    ``build_ragged_grid`` over cu_seqlens_q and cu_seqlens_k with the kernel's
+    block_m; then ``row_stats`` (fp32 [2, H, rows_q]) carries the row
+    statistics from the dq phase to the dk/dv phase and ``phases`` selects
+    VLP_BWD_DQ, VLP_BWD_DKDV or both.
     """
     lib = _lib.load()
     tensors = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k)
@@ -263,6 +272,22 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     code = _DTYPE_CODES[q.dtype]
+    if grids is not None:
+        gq, gk = grids
+        if row_stats is None:
+            row_stats = torch.empty(2, heads, rows_q, dtype=torch.float32, device=q.device)
+
+        def nblocks(g):
+            return g.num_blocks if g.num_blocks is not None else int(g.grid_mapping.numel())
+        st = lib.vlp_varlen_attn_bwd_grid(code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, rows_q, total_k, heads,
+                                          head_dim, int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(gq.grid_mapping), _ptr(gq.block_offsets),
+                                          _ptr(gq.tile_order), nblocks(gq), _ptr(gk.grid_mapping),
+                                          _ptr(gk.block_offsets), _ptr(gk.tile_order), nblocks(gk), gq.block_m,
+                                          _ptr(row_stats), int(phases), _stream_handle(q.device))
+        _lib.check(st, "varlen_attn_bwd_grid")
+        return dq, dk, dv
     if workspace is None:
         bm = lib.vlp_kernel_block_m(code, head_dim, int(bool(causal)), 0, b, rows_q, int(max_seqlen))
         if bm < 1:

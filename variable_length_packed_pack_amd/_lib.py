@@ -26,6 +26,8 @@ VLP_BF16 = 2
 
 VLP_FIRST_TOKEN_BLOCK_M = 1 << 30
 VLP_DEVICE_SORT_MAX_SEQS = 4096
+VLP_BWD_DQ = 1
+VLP_BWD_DKDV = 2
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -56,6 +58,11 @@ SIGNATURES = {
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "vlp_varlen_attn_bwd_grid": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                                  _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp, _vp,
+                                                  ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 

@@ -260,6 +260,54 @@ extern "C" vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64
   return VLP_OK;
 }
 
+namespace {
+
+// Shared validation of the backward arguments (the forward's plus the
+// gradient buffers).
+vlp_status check_backward(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, const int32_t* cu_q, const int32_t* cu_k,
+                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads, int32_t head_dim,
+                          int32_t max_seqlen, float scale, int32_t causal, const void* dq, const void* dk,
+                          const void* dv, Checked* c) {
+  vlp_status st = check_forward(dtype, q, k, v, cu_q, cu_k, num_seqs, rows_q, total_k, heads, head_dim, max_seqlen,
+                                scale, causal, 0, out, c);
+  if (st != VLP_OK) return st;
+  if (!dout || !lse || !dq || !dk || !dv) return VLP_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return VLP_ERR_INVALID;
+  if (rows_q * heads > INT32_MAX || total_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  return VLP_OK;
+}
+
+vlp::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                           const float* lse, const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
+                           int64_t rows_q, int32_t heads, float scale, void* dq, void* dk, void* dv,
+                           float* row_stats) {
+  vlp::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.lse2 = row_stats;
+  a.delta = row_stats + static_cast<size_t>(heads) * static_cast<size_t>(rows_q);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.heads = heads;
+  a.rows_q = static_cast<int32_t>(rows_q);
+  a.scale = scale;
+  a.scale_log2 = exp2_factor(scale);
+  return a;
+}
+
+}  // namespace
+
 extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
                                           const void* out, const void* dout, const float* lse,
                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -268,39 +316,20 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
                                           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                           void* stream) {
   Checked c{};
-  vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
-                                head_dim, max_seqlen, scale, causal, 0, out, &c);
+  vlp_status st = check_backward(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q,
+                                 total_k, heads, head_dim, max_seqlen, scale, causal, dq, dk, dv, &c);
   if (st != VLP_OK) return st;
-  if (!dout || !lse || !dq || !dk || !dv || !workspace) return VLP_ERR_NULL;
-  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return VLP_ERR_INVALID;
-  if (rows_q * heads > INT32_MAX || total_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  if (!workspace) return VLP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
   const BwdWorkspace w = bwd_workspace(num_seqs, rows_q, total_k, heads, c.block_m);
   if (w.cap_q * heads > INT32_MAX || w.cap_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
   if (workspace_bytes < w.bytes) return VLP_ERR_CAPACITY;
 
   char* base = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  vlp::BwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.dout = dout;
-  a.lse = lse;
-  a.lse2 = reinterpret_cast<float*>(base + w.off_lse2);
+  vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
+                                 scale, dq, dk, dv, reinterpret_cast<float*>(base + w.off_lse2));
   a.delta = reinterpret_cast<float*>(base + w.off_delta);
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.cu_q = cu_seqlens_q;
-  a.cu_k = cu_seqlens_k;
-  a.num_seqs = num_seqs;
-  a.heads = heads;
-  a.rows_q = static_cast<int32_t>(rows_q);
-  a.scale = scale;
-  a.scale_log2 = exp2_factor(scale);
 
   // dQ over the query grid first: it also writes lse2 and delta, which the
   // dK/dV launch (same stream) reads.
@@ -330,6 +359,48 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
     a.tile_order = to;
     a.grid_cap = static_cast<int32_t>(w.cap_k);
     st = launch_bwd(dtype, true, a, head_dim, causal != 0, w.cap_k * heads, s);
+  }
+  return st;
+}
+
+extern "C" vlp_status vlp_varlen_attn_bwd_grid(
+    int32_t dtype, const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+    int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal, void* dq, void* dk, void* dv,
+    const int32_t* q_grid_mapping, const int32_t* q_block_offsets, const int32_t* q_tile_order,
+    int64_t q_num_blocks, const int32_t* k_grid_mapping, const int32_t* k_block_offsets,
+    const int32_t* k_tile_order, int64_t k_num_blocks, int32_t block_m, float* row_stats, int32_t phases,
+    void* stream) {
+  Checked c{};
+  vlp_status st = check_backward(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q,
+                                 total_k, heads, head_dim, max_seqlen, scale, causal, dq, dk, dv, &c);
+  if (st != VLP_OK) return st;
+  if (phases < 1 || phases > 3) return VLP_ERR_INVALID;
+  const bool run_dq = (phases & VLP_BWD_DQ) != 0, run_dkdv = (phases & VLP_BWD_DKDV) != 0;
+  if (!row_stats) return VLP_ERR_NULL;
+  if (run_dq && (!q_grid_mapping || !q_block_offsets)) return VLP_ERR_NULL;
+  if (run_dkdv && (!k_grid_mapping || !k_block_offsets)) return VLP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(row_stats) & 3u) != 0) return VLP_ERR_INVALID;
+  if (block_m != c.block_m || (run_dq && q_num_blocks < 0) || (run_dkdv && k_num_blocks < 0)) return VLP_ERR_INVALID;
+  if ((run_dq && q_num_blocks * heads > INT32_MAX) || (run_dkdv && k_num_blocks * heads > INT32_MAX))
+    return VLP_ERR_OVERFLOW;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
+                                 scale, dq, dk, dv, row_stats);
+  if (run_dq) {
+    a.grid_mapping = q_grid_mapping;
+    a.block_offsets = q_block_offsets;
+    a.tile_order = q_tile_order;
+    a.grid_cap = static_cast<int32_t>(q_num_blocks);
+    st = launch_bwd(dtype, false, a, head_dim, causal != 0, q_num_blocks * heads, s);
+    if (st != VLP_OK) return st;
+  }
+  if (run_dkdv) {
+    a.grid_mapping = k_grid_mapping;
+    a.block_offsets = k_block_offsets;
+    a.tile_order = k_tile_order;
+    a.grid_cap = static_cast<int32_t>(k_num_blocks);
+    st = launch_bwd(dtype, true, a, head_dim, causal != 0, k_num_blocks * heads, s);
   }
   return st;
 }
