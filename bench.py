@@ -336,8 +336,11 @@ def bench_backward(args, wl, dev) -> int:
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # each kernel alone: cached grids, HIP events on the stream they run on
-    gh = vlp.build_ragged_grid(cu_host, bm)
-    grid = vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev), gh.tile_order.to(dev), gh.num_blocks, bm)
+    def dev_grid(block):
+        gh = vlp.build_ragged_grid(cu_host, block)
+        return vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev), gh.tile_order.to(dev),
+                              gh.num_blocks, block)
+    grids = (dev_grid(bm), dev_grid(vlp.VLP_BWD_BLOCK_K))
     stats = torch.empty(2, h, t, dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
     reps = args.kernel_only_reps or args.steps
@@ -345,16 +348,16 @@ def bench_backward(args, wl, dev) -> int:
     kernel_ms = {}
     with torch.cuda.stream(stream):
         vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk, dv,
-                            grids=(grid, grid), row_stats=stats, phases=vlp.VLP_BWD_DQ | vlp.VLP_BWD_DKDV)
+                            grids=grids, row_stats=stats, phases=vlp.VLP_BWD_DQ | vlp.VLP_BWD_DKDV)
         for name, ph in (("dkdv", vlp.VLP_BWD_DKDV), ("dq", vlp.VLP_BWD_DQ)):
             for _ in range(2):
                 vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk,
-                                    dv, grids=(grid, grid), row_stats=stats, phases=ph)
+                                    dv, grids=grids, row_stats=stats, phases=ph)
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
             for _ in range(reps):
                 vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, dq, dk,
-                                    dv, grids=(grid, grid), row_stats=stats, phases=ph)
+                                    dv, grids=grids, row_stats=stats, phases=ph)
             ev1.record(stream)
             stream.synchronize()
             kernel_ms[name] = ev0.elapsed_time(ev1) / reps

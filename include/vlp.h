@@ -254,11 +254,18 @@ vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k,
                                     void* stream);
 
 /*
+ * Key rows per tile of the key grid that the dk/dv kernel of the backward
+ * walks (for every dtype and head_dim).
+ */
+#define VLP_BWD_BLOCK_K 64
+
+/*
  * vlp_varlen_attn_bwd_workspace_size -- bytes of device workspace that
  * vlp_varlen_attn_bwd needs: two fp32 [heads, rows_q] row statistics plus a
  * device-built grid over the query lengths and one over the key lengths
- * (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k, num_seqs, block_m)
- * tiles), block_m = vlp_kernel_block_m(dtype, head_dim, causal, 0, ...).
+ * (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k, num_seqs,
+ * VLP_BWD_BLOCK_K) tiles), block_m = vlp_kernel_block_m(dtype, head_dim,
+ * causal, 0, ...).
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, total_k < 0,
  * heads < 1, block_m < 1 -> VLP_ERR_INVALID; rows beyond int32 ->
  * VLP_ERR_OVERFLOW.
@@ -319,9 +326,11 @@ vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, cons
  *                  may be NULL: natural order); q_num_blocks * heads
  *                  workgroups run the dq phase.
  *   k_grid_mapping, k_block_offsets, k_tile_order, k_num_blocks
- *                  the same for cu_seqlens_k; they run the dk/dv phase.
- *   block_m        must equal vlp_kernel_block_m(dtype, head_dim, causal, 0,
- *                  ...); both grids use it.
+ *                  the ragged grid of cu_seqlens_k built with block_m =
+ *                  VLP_BWD_BLOCK_K; k_num_blocks * heads workgroups run the
+ *                  dk/dv phase.
+ *   block_m        the query grid's; must equal vlp_kernel_block_m(dtype,
+ *                  head_dim, causal, 0, ...).
  *   row_stats      device fp32 [2, heads, rows_q], 4-byte aligned: written by
  *                  the dq phase (the log-sum-exp in base-2 units and
  *                  rowsum(dout * out) of every owned query row), read by the

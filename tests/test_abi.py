@@ -50,6 +50,7 @@ def test_header_constants_match_binding():
     assert f"#define VLP_DEVICE_SORT_MAX_SEQS {_lib.VLP_DEVICE_SORT_MAX_SEQS}" in text
     assert "#define VLP_FIRST_TOKEN_BLOCK_M (1 << 30)" in text
     assert f"#define VLP_BWD_DQ {_lib.VLP_BWD_DQ}" in text and f"#define VLP_BWD_DKDV {_lib.VLP_BWD_DKDV}" in text
+    assert f"#define VLP_BWD_BLOCK_K {_lib.VLP_BWD_BLOCK_K}" in text
     for name in ("VLP_FP32 = 0", "VLP_FP16 = 1", "VLP_BF16 = 2", "VLP_OK = 0", "VLP_ERR_HIP = 6"):
         assert name in text
 
@@ -319,7 +320,7 @@ def test_backward_workspace_size():
     assert lib.vlp_varlen_attn_bwd_workspace_size(4, 10, 10, 1, 0, ctypes.addressof(n)) == 2
     assert lib.vlp_varlen_attn_bwd_workspace_size(64, 65536, 70000, 16, 128, ctypes.addressof(n)) == 0
     cq = vlp.grid_capacity(65536, 64, 128)
-    ck = vlp.grid_capacity(70000, 64, 128)
+    ck = vlp.grid_capacity(70000, 64, vlp.VLP_BWD_BLOCK_K)
     assert n.value >= 2 * 4 * 16 * 65536 + 4 * (2 * 65 + 2 * cq + 2 * ck)
     assert n.value == vlp.bwd_workspace_size(64, 65536, 70000, 16, 128)
 

@@ -229,11 +229,14 @@ def test_bwd_cached_grids_phases_and_tile_order_bitwise():
     cud = cu.to(DEV)
     out, lse = vlp.varlen_attn_fwd(q, k, v, cud, cud, 0, wl.scale, True)
     ref = vlp.varlen_attn_bwd(q, k, v, out, do, lse, cud, cud, 0, wl.scale, True)
-    bm = vlp.kernel_block_m(q.dtype, d, True)
-    gh = vlp.build_ragged_grid(cu, bm)
-    g = vlp.RaggedGrid(gh.grid_mapping.to(DEV), gh.block_offsets.to(DEV), gh.tile_order.to(DEV), gh.num_blocks, bm)
-    natural = g._replace(tile_order=None)
-    for grids, phases in (((g, g), (3,)), ((g, g), (1, 2)), ((natural, natural), (3,))):
+    def dev_grid(block):
+        gh = vlp.build_ragged_grid(cu, block)
+        return vlp.RaggedGrid(gh.grid_mapping.to(DEV), gh.block_offsets.to(DEV), gh.tile_order.to(DEV),
+                              gh.num_blocks, block)
+    gq = dev_grid(vlp.kernel_block_m(q.dtype, d, True))
+    gk = dev_grid(vlp.VLP_BWD_BLOCK_K)
+    nq, nk = gq._replace(tile_order=None), gk._replace(tile_order=None)
+    for grids, phases in (((gq, gk), (3,)), ((gq, gk), (1, 2)), ((nq, nk), (3,))):
         dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
         stats = torch.empty(2, h, q.shape[0], dtype=torch.float32, device=DEV)
         for ph in phases:

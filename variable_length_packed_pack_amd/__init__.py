@@ -30,6 +30,7 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     VLP_BF16,
+    VLP_BWD_BLOCK_K,
     VLP_BWD_DKDV,
     VLP_BWD_DQ,
     VLP_DEVICE_SORT_MAX_SEQS,
@@ -242,8 +243,8 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     ``dout`` has the shape of ``out``.  Rows owned by no sequence are never
     written (fresh outputs are allocated with ``torch.empty``).
     ``grids``: cached device metadata ``(query_grid, key_grid)`` from
-    ``build_ragged_grid`` over cu_seqlens_q and cu_seqlens_k with the kernel's
-    block_m; then ``row_stats`` (fp32 [2, H, rows_q]) carries the row
+    ``build_ragged_grid`` over cu_seqlens_q with the kernel's block_m and over
+    cu_seqlens_k with VLP_BWD_BLOCK_K; then ``row_stats`` (fp32 [2, H, rows_q]) carries the row
     statistics from the dq phase to the dk/dv phase and ``phases`` selects
     VLP_BWD_DQ, VLP_BWD_DKDV or both.
     """

@@ -28,6 +28,7 @@ VLP_FIRST_TOKEN_BLOCK_M = 1 << 30
 VLP_DEVICE_SORT_MAX_SEQS = 4096
 VLP_BWD_DQ = 1
 VLP_BWD_DKDV = 2
+VLP_BWD_BLOCK_K = 64
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)

@@ -118,7 +118,7 @@ BwdWorkspace bwd_workspace(int32_t num_seqs, int64_t rows_q, int64_t total_k, in
   BwdWorkspace w;
   const size_t stats = round_up(sizeof(float) * static_cast<size_t>(heads) * static_cast<size_t>(rows_q), 256);
   w.cap_q = vlp_grid_capacity(rows_q, num_seqs, block);
-  w.cap_k = vlp_grid_capacity(total_k, num_seqs, block);
+  w.cap_k = vlp_grid_capacity(total_k, num_seqs, VLP_BWD_BLOCK_K);
   w.qg = grid_workspace(num_seqs, w.cap_q);
   w.kg = grid_workspace(num_seqs, w.cap_k);
   w.off_lse2 = 0;
@@ -352,7 +352,7 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
     int32_t* bo = reinterpret_cast<int32_t*>(g + w.kg.off_bo);
     int32_t* gm = reinterpret_cast<int32_t*>(g + w.kg.off_gm);
     int32_t* to = reinterpret_cast<int32_t*>(g + w.kg.off_to);
-    st = hip_status(vlp::launch_grid_build(cu_seqlens_k, num_seqs, c.block_m, bo, gm, to, w.cap_k, s));
+    st = hip_status(vlp::launch_grid_build(cu_seqlens_k, num_seqs, VLP_BWD_BLOCK_K, bo, gm, to, w.cap_k, s));
     if (st != VLP_OK) return st;
     a.grid_mapping = gm;
     a.block_offsets = bo;

@@ -9,6 +9,7 @@ template <int D, bool CAUSAL, bool DKDV>
 hipError_t go(const BwdArgs& a, int64_t blocks, hipStream_t s) {
   constexpr int NW = tile_waves(VLP_FP32, D);
   constexpr int BN = tile_block_n(VLP_FP32, D);  // keys (dQ) or queries (dK/dV) per streamed block
+  static_assert(32 * NW == VLP_BWD_BLOCK_K, "the dK/dV kernel covers one tile of the key grid");
   if (DKDV)
     hipLaunchKernelGGL((attn_bwd_dkdv_f32<D, NW, BN, CAUSAL>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
                        0, s, a);

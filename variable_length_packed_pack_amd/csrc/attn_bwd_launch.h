@@ -21,7 +21,7 @@ hipError_t bwd_dq_go(const BwdArgs& a, int64_t blocks, hipStream_t s) {
 
 template <int DT, int D, bool CAUSAL>
 hipError_t bwd_dkdv_go(const BwdArgs& a, int64_t blocks, hipStream_t s) {
-  constexpr int NW = tile_waves(DT, D);
+  constexpr int NW = VLP_BWD_BLOCK_K / 32;  // key tiles of the key grid
   hipLaunchKernelGGL((attn_bwd_dkdv_h16<DT, D, NW, kBwdBlockQ, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(NW * 64), 0, s, a);
   return hipGetLastError();

@@ -111,6 +111,16 @@ __device__ __forceinline__ void mma_rows(const char* tile, const int (&yoff)[KS]
       const u32x4_t yop = *reinterpret_cast<const u32x4_t*>(tile + 32 * i * RB + yoff[k]);
       acc[i] = E::mfma(yop, xv[k], acc[i]);
     }
+  // Operand reads AHEAD MFMAs ahead of their use: an LDS read takes several
+  // MFMA issue slots to return.
+  constexpr int NM = KS * NS;
+  constexpr int AHEAD = NM < 4 ? NM : 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int t = 0; t < NM; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (t + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next read
+  }
 }
 
 // acc[d] += Y^T W: A = the Y tile read transposed (offsets ytoff, as the
@@ -140,6 +150,15 @@ __device__ __forceinline__ void mma_tr(const char* tile, const int (&ytoff)[2][D
         acc[d] = E::mfma(yop, wop, acc[d]);
       }
     }
+  // Two transposing reads per MFMA, issued AHEAD MFMAs ahead.
+  constexpr int NM = NS * 2 * DT32;
+  constexpr int AHEAD = NM < 3 ? NM : 3;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+  for (int t = 0; t < NM; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (t + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
 }
 
 // Operand offsets shared by both kernels (bytes within one tile).
@@ -346,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
 template <int DT, int D, int NW, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(const BwdArgs a) {
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head_dim");
-  static_assert(BQ == 64, "one 4-byte direct load moves the 64 row statistics of a query block");
+  static_assert(BQ % 64 == 0, "4-byte direct loads move the row statistics 64 rows at a time");
   constexpr int BK = 32 * NW;
   constexpr int KS = D / 16;
   constexpr int DT32 = (D + 31) / 32;
@@ -431,12 +450,16 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
     }
     if (wave == 0) {
-      // 64 lanes x 4 bytes: the block's lse2 and delta (zeros past the end).
+      // 64 lanes x 4 bytes per load: the block's lse2 and delta (zeros past
+      // the end).
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(a.lse2 + stat0 + qb, 0, nrows * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t rdl = __builtin_amdgcn_make_buffer_rsrc(a.delta + stat0 + qb, 0, nrows * 4, 0x00020000);
-      const int lo = lane * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (VLP_LDS void*)(buf + STATS), 4, lo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdl, (VLP_LDS void*)(buf + STATS + 4 * BQ), 4, lo, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < BQ / 64; ++j) {
+        const int lo = lane * 4 + 256 * j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (VLP_LDS void*)(buf + STATS + 256 * j), 4, lo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdl, (VLP_LDS void*)(buf + STATS + 4 * BQ + 256 * j), 4, lo, 0, 0, 0);
+      }
     }
   };
 
