@@ -184,10 +184,10 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  *
  *   dtype          VLP_FP32, VLP_FP16 or VLP_BF16 for q, k, v and out; the
  *                  contractions accumulate in fp32, the softmax runs in fp32.
- *   q              device [rows_q, heads, head_dim], contiguous; in
- *                  first-token mode rows_q == num_seqs and row i is the query
- *                  of sequence i (the page's query[cu_seqlens[:-1]]).
- *   k, v           device [total_k, heads, head_dim], contiguous.
+ *   q              device [rows_q, heads, head_dim]; in first-token mode
+ *                  rows_q == num_seqs and row i is the query of sequence i
+ *                  (the page's query[cu_seqlens[:-1]]).
+ *   k, v           device [total_k, heads, head_dim].
  *   cu_seqlens_q   device int32 [num_seqs + 1] (ignored, may be NULL, in
  *                  first-token mode).
  *   cu_seqlens_k   device int32 [num_seqs + 1]; cu[0] = 0, non-decreasing,
@@ -200,6 +200,17 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  *   total_k        physical key rows.
  *   heads, head_dim  heads >= 1; head_dim in {16, 32, 64, 128} ("head_dim must
  *                  be a multiple of 8"; these four are built).
+ *   q_row_stride, kv_row_stride, out_row_stride
+ *                  elements between consecutive tokens of q, of k and v (one
+ *                  stride shared by both), and of out; within a token the
+ *                  heads are head_dim elements apart and each head's
+ *                  head_dim elements are contiguous.  0 = heads * head_dim
+ *                  (contiguous).  Larger strides take views into a fused
+ *                  projection output, e.g. q, k, v = qkv.view(T, 3, H, D)
+ *                  .unbind(1) with stride 3 * H * D ("PyCoRa", "Ragged Flash
+ *                  Attention": the attention module passes such unbound
+ *                  views).  Each must be >= heads * head_dim, give 16-byte
+ *                  aligned rows, and stride * element size <= 2^24 bytes.
  *   max_seqlen     a hint (0 = unknown); never needed for correctness.
  *   scale          finite softmax scale >= 0 (usually 1/sqrt(head_dim)); the
  *                  running row maximum is taken on the unscaled scores.
@@ -216,14 +227,17 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  * Errors: NULL q/k/v/out/cu_seqlens_k/workspace (or cu_seqlens_q outside
  * first-token mode) -> VLP_ERR_NULL; dtype or head_dim not built ->
  * VLP_ERR_UNSUPPORTED; num_seqs < 1, heads < 1, rows_q < 0, total_k < 0,
- * non-finite or negative scale, misaligned pointers, rows_q != num_seqs in first-token
- * mode -> VLP_ERR_INVALID; rows or rows*heads beyond int32 -> VLP_ERR_OVERFLOW;
- * small workspace -> VLP_ERR_CAPACITY; launch failure -> VLP_ERR_HIP.
+ * non-finite or negative scale, misaligned pointers, a stride below heads *
+ * head_dim or not giving 16-byte aligned rows, rows_q != num_seqs in
+ * first-token mode -> VLP_ERR_INVALID; rows or rows*heads beyond int32, a
+ * stride beyond 2^24 bytes -> VLP_ERR_OVERFLOW; small workspace ->
+ * VLP_ERR_CAPACITY; launch failure -> VLP_ERR_HIP.
  */
 vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int32_t num_seqs, int64_t rows_q, int64_t total_k,
-                               int32_t heads, int32_t head_dim, int32_t max_seqlen,
+                               int32_t heads, int32_t head_dim, int64_t q_row_stride,
+                               int64_t kv_row_stride, int64_t out_row_stride, int32_t max_seqlen,
                                float scale, int32_t causal, int32_t query_is_first_token,
                                void* out, float* lse, void* workspace, size_t workspace_bytes,
                                void* stream);
@@ -246,7 +260,8 @@ vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, cons
 vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k, const void* v,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                     int32_t num_seqs, int64_t rows_q, int64_t total_k,
-                                    int32_t heads, int32_t head_dim, int32_t max_seqlen,
+                                    int32_t heads, int32_t head_dim, int64_t q_row_stride,
+                                    int64_t kv_row_stride, int64_t out_row_stride, int32_t max_seqlen,
                                     float scale, int32_t causal, int32_t query_is_first_token,
                                     void* out, float* lse,
                                     const int32_t* grid_mapping, const int32_t* block_offsets,
@@ -290,8 +305,12 @@ vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, 
  *   dtype          VLP_FP32, VLP_FP16 or VLP_BF16; fp32 accumulation,
  *                  gradients rounded to dtype.
  *   q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
- *   head_dim, max_seqlen, scale, causal   as for vlp_varlen_attn_fwd (no
- *                  first-token mode).
+ *   head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen,
+ *   scale, causal  as for vlp_varlen_attn_fwd (no first-token mode).
+ *   dout_row_stride, dq_row_stride, dkv_row_stride
+ *                  token strides of dout, of dq, and of dk and dv (one
+ *                  stride shared by both), with the same rules; views into
+ *                  one fused gradient buffer are allowed.
  *   out            device [rows_q, heads, head_dim], the forward's output.
  *   dout           device [rows_q, heads, head_dim], gradient of the output.
  *   lse            device fp32 [heads, rows_q], the forward's log-sum-exp.
@@ -304,6 +323,8 @@ vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, 
  *   workspace      device, >= vlp_varlen_attn_bwd_workspace_size bytes,
  *                  256-byte aligned; overwritten.
  * q, k, v, out, dout, dq, dk and dv must be 16-byte aligned, lse 4-byte.
+ * dq, dk and dv must not overlap any input or each other's elements (they
+ * may be disjoint views into one buffer).
  * Errors: as vlp_varlen_attn_fwd, plus NULL dout/lse/dq/dk/dv/workspace ->
  * VLP_ERR_NULL, misaligned dout/dq/dk/dv/lse/workspace -> VLP_ERR_INVALID,
  * small workspace -> VLP_ERR_CAPACITY.
@@ -311,7 +332,9 @@ vlp_status vlp_varlen_attn_bwd_workspace_size(int32_t num_seqs, int64_t rows_q, 
 vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
                                const void* dout, const float* lse, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
-                               int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                               int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                               int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
+                               int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal,
                                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -348,7 +371,9 @@ vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, cons
 vlp_status vlp_varlen_attn_bwd_grid(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
                                     const void* dout, const float* lse, const int32_t* cu_seqlens_q,
                                     const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
-                                    int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale,
+                                    int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                    int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
+                                    int64_t dkv_row_stride, int32_t max_seqlen, float scale,
                                     int32_t causal, void* dq, void* dk, void* dv, const int32_t* q_grid_mapping,
                                     const int32_t* q_block_offsets, const int32_t* q_tile_order,
                                     int64_t q_num_blocks, const int32_t* k_grid_mapping,

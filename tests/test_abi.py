@@ -206,11 +206,13 @@ FAKE = 0x10000  # aligned, never dereferenced: each case fails validation first
 def _fwd(**kw):
     lib = _lib.load()
     a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100, total_k=100, heads=2,
-             head_dim=64, max_seqlen=0, scale=0.125, causal=0, ft=0, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 20)
+             head_dim=64, qs=0, kvs=0, os=0, max_seqlen=0, scale=0.125, causal=0, ft=0, out=FAKE, lse=None, ws=FAKE,
+             ws_bytes=1 << 20)
     a.update(kw)
     return lib.vlp_varlen_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["b"], a["rows_q"],
-                                   a["total_k"], a["heads"], a["head_dim"], a["max_seqlen"], a["scale"],
-                                   a["causal"], a["ft"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+                                   a["total_k"], a["heads"], a["head_dim"], a["qs"], a["kvs"], a["os"],
+                                   a["max_seqlen"], a["scale"], a["causal"], a["ft"], a["out"], a["lse"], a["ws"],
+                                   a["ws_bytes"], None)
 
 
 def test_forward_validation_errors():
@@ -236,6 +238,13 @@ def test_forward_validation_errors():
     assert _fwd(rows_q=2**31) == 5
     assert _fwd(rows_q=2**30, heads=4) == 5
     assert _fwd(ws_bytes=16) == 4
+    # token strides: 0 = contiguous; >= heads*head_dim; 16-byte rows; <= 2^24 bytes
+    assert _fwd(qs=128, kvs=384, os=128, ws_bytes=16) == 4   # valid strides reach the workspace check
+    assert _fwd(qs=127) == 2                    # below heads * head_dim
+    assert _fwd(kvs=132) == 2                   # 264-byte rows: not 16-byte aligned
+    assert _fwd(os=-1) == 2
+    assert _fwd(dtype=0, qs=130) == 2           # fp32: 520-byte rows are not 16-byte aligned
+    assert _fwd(qs=(1 << 23) + 8) == 5          # beyond 2^24 bytes per token
 
 
 def test_grid_forward_validation_errors():
@@ -244,26 +253,27 @@ def test_grid_forward_validation_errors():
     def call(**kw):
         a = dict(gm=FAKE, bo=FAKE, to=None, nb=3, bm=lib.vlp_kernel_block_m(2, 128, 0, 0, 4, 100, 0), head_dim=128)
         a.update(kw)
-        return lib.vlp_varlen_attn_fwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, a["head_dim"], 0,
-                                            0.1, 0, 0, FAKE, None, a["gm"], a["bo"], a["to"], a["nb"], a["bm"],
-                                            None)
+        return lib.vlp_varlen_attn_fwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, a["head_dim"], 0, 0,
+                                            a.get("os", 0), 0, 0.1, 0, 0, FAKE, None, a["gm"], a["bo"], a["to"],
+                                            a["nb"], a["bm"], None)
     assert call(gm=None) == 1
     assert call(bo=None) == 1
     assert call(nb=-1) == 2
     assert call(bm=64) == 2                      # must equal vlp_kernel_block_m
     assert call(nb=2**31) == 5
+    assert call(os=100) == 2
 
 
 def _bwd(**kw):
     lib = _lib.load()
     a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100,
-             total_k=100, heads=2, head_dim=64, max_seqlen=0, scale=0.125, causal=0, dq=FAKE, dk=FAKE, dv=FAKE,
-             ws=FAKE, ws_bytes=1 << 20)
+             total_k=100, heads=2, head_dim=64, strides=(0, 0, 0, 0, 0, 0), max_seqlen=0, scale=0.125, causal=0,
+             dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 20)
     a.update(kw)
     return lib.vlp_varlen_attn_bwd(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["cu_q"],
                                    a["cu_k"], a["b"], a["rows_q"], a["total_k"], a["heads"], a["head_dim"],
-                                   a["max_seqlen"], a["scale"], a["causal"], a["dq"], a["dk"], a["dv"], a["ws"],
-                                   a["ws_bytes"], None)
+                                   *a["strides"], a["max_seqlen"], a["scale"], a["causal"], a["dq"], a["dk"],
+                                   a["dv"], a["ws"], a["ws_bytes"], None)
 
 
 def test_backward_validation_errors():
@@ -284,6 +294,11 @@ def test_backward_validation_errors():
     assert _bwd(rows_q=2**31) == 5
     assert _bwd(total_k=2**30, heads=4) == 5
     assert _bwd(ws_bytes=64) == 4
+    assert _bwd(strides=(384, 384, 128, 128, 384, 384), ws_bytes=64) == 4   # fused q/k/v and dq/dk/dv views
+    for i in range(6):
+        bad = [0] * 6
+        bad[i] = 120
+        assert _bwd(strides=tuple(bad)) == 2, i
 
 
 def test_grid_backward_validation_errors():
@@ -294,7 +309,8 @@ def test_grid_backward_validation_errors():
         a = dict(qgm=FAKE, qbo=FAKE, qn=3, kgm=FAKE, kbo=FAKE, kn=3, bm=bm, stats=FAKE, phases=3, dq=FAKE)
         a.update(kw)
         return lib.vlp_varlen_attn_bwd_grid(2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, 100, 2, 64,
-                                            0, 0.1, 0, a["dq"], FAKE, FAKE, a["qgm"], a["qbo"], None, a["qn"],
+                                            0, 0, 0, 0, 0, 0, 0, 0.1, 0, a["dq"], FAKE, FAKE, a["qgm"], a["qbo"], None,
+                                            a["qn"],
                                             a["kgm"], a["kbo"], None, a["kn"], a["bm"], a["stats"], a["phases"],
                                             None)
     assert call(dq=None) == 1

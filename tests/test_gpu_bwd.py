@@ -26,6 +26,7 @@ forward's output, plus 2^-14 of the row's largest element for the
 accumulation over long rows.
 """
 
+import math
 import sys
 
 import numpy as np
@@ -245,6 +246,36 @@ def test_bwd_cached_grids_phases_and_tile_order_bitwise():
         torch.cuda.synchronize()
         for x, y in zip((dq, dk, dv), ref):
             assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_bwd_strided_views_of_fused_buffers(dtype, head_dim):
+    """q, k, v from one [T, 3, H, D] projection, dout a view into a wider
+    buffer, dq/dk/dv written into views of one [T, 3, H, D] gradient buffer:
+    bit-identical to contiguous tensors, and nothing outside the views is
+    written."""
+    lengths = [1, 200, 64, 129, 3, 77]
+    t, h = sum(lengths), 2
+    tdt = workloads.DTYPES[dtype]
+    g = torch.Generator().manual_seed(40 + head_dim)
+    qkv = torch.randn(t, 3, h, head_dim, generator=g).to(tdt).to(DEV)
+    dwide = torch.randn(t, 2, h, head_dim, generator=g).to(tdt).to(DEV)
+    q, k, v = qkv.unbind(1)
+    do = dwide[:, 1]
+    cu = _cu(lengths).to(DEV)
+    scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    for causal in (False, True):
+        qc, kc, vc, doc = q.contiguous(), k.contiguous(), v.contiguous(), do.contiguous()
+        out, lse = vlp.varlen_attn_fwd(qc, kc, vc, cu, cu, 0, scale, causal)
+        ref = vlp.varlen_attn_bwd(qc, kc, vc, out, doc, lse, cu, cu, 0, scale, causal)
+        dqkv = torch.full((t, 3, h, head_dim), float("nan"), dtype=tdt, device=DEV)
+        dq, dk, dv = dqkv.unbind(1)
+        vlp.varlen_attn_bwd(q, k, v, out, do, lse, cu, cu, 0, scale, causal, dq, dk, dv)
+        torch.cuda.synchronize()
+        for x, y in zip((dq, dk, dv), ref):
+            assert torch.equal(x, y)
+        assert not torch.isnan(dqkv.float()).any().item()
 
 
 # --------------------------------------------------------------------------

@@ -285,6 +285,37 @@ def test_zero_scale_gives_uniform_weights(dtype):
         assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= TOL_LSE
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_strided_views_of_a_fused_projection(dtype, head_dim):
+    """q, k, v as views of one [T, 3, H, D] projection output and out as a
+    view into a wider buffer give bit-identical results to contiguous
+    copies (the kernels only address rows differently)."""
+    lengths = [1, 200, 64, 129, 3, 77]
+    t, h = sum(lengths), 3
+    tdt = workloads.DTYPES[dtype]
+    g = torch.Generator().manual_seed(30 + head_dim)
+    qkv = torch.randn(t, 3, h, head_dim, generator=g).to(tdt).to(DEV)
+    q, k, v = qkv.unbind(1)
+    assert not q.is_contiguous() and q.stride(0) == 3 * h * head_dim
+    cu = _cu(lengths).to(DEV)
+    scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    for causal in (False, True):
+        ref_out, ref_lse = vlp.varlen_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), cu, cu, 0, scale,
+                                               causal)
+        wide = torch.full((t, 2, h, head_dim), float("nan"), dtype=tdt, device=DEV)
+        out, lse = vlp.varlen_attn_fwd(q, k, v, cu, cu, 0, scale, causal, out=wide[:, 1])
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+        assert torch.isnan(wide[:, 0].float()).all().item()  # the other half of the buffer is untouched
+    # first-token mode: one query per sequence, k and v still strided views
+    qf = q[cu[:-1].long()].contiguous()
+    ref_out, ref_lse = vlp.varlen_attn_fwd(qf, k.contiguous(), v.contiguous(), None, cu, 0, scale, False, True)
+    out, lse = vlp.varlen_attn_fwd(qf, k, v, None, cu, 0, scale, False, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
 def test_causal_with_longer_keys():
     """Lq != Lk (cross-attention shapes): bottom-right causal alignment."""
     rng = np.random.default_rng(14)

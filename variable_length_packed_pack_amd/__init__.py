@@ -47,6 +47,17 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _token_stride(t: torch.Tensor, name: str) -> int:
+    """Elements between consecutive tokens of a [rows, H, D] tensor whose
+    heads are D apart and whose head rows are contiguous (a contiguous tensor
+    or a view such as qkv.view(T, 3, H, D).unbind(1)); raises otherwise."""
+    if t.dim() != 3 or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{name}: heads must be head_dim apart and each head row contiguous")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1] * t.shape[2]:
+        raise ValueError(f"{name}: tokens overlap")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1] * t.shape[2])  # one row: any stride
+
+
 def _stream_handle(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -177,9 +188,9 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise TypeError("q, k, v must share one of float32 / float16 / bfloat16")
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
         raise ValueError("q [rows, H, D] and k, v [T, H, D] with matching H, D")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
+    q_st, k_st, v_st = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if k_st != v_st and k.shape[0] > 1:
+        raise ValueError("k and v must share one token stride")
     rows_q, heads, head_dim = (int(x) for x in q.shape)
     total_k = int(k.shape[0])
     b = int(cu_seqlens_k.numel()) - 1
@@ -189,7 +200,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         scale = float(np.float32(1.0 / math.sqrt(head_dim)))
     dev = q.device
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    o_st = _token_stride(out, "out")
     if lse is None and return_lse:
         lse = torch.empty(heads, rows_q, dtype=torch.float32, device=dev)
     code = _DTYPE_CODES[q.dtype]
@@ -199,7 +211,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if grid is not None:
         nb = grid.num_blocks if grid.num_blocks is not None else int(grid.grid_mapping.numel())
         st = lib.vlp_varlen_attn_fwd_grid(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b,
-                                          rows_q, total_k, heads, head_dim, int(max_seqlen), float(scale),
+                                          rows_q, total_k, heads, head_dim, q_st, k_st, o_st, int(max_seqlen),
+                                          float(scale),
                                           int(bool(causal)), ft, _ptr(out), _ptr(lse), _ptr(grid.grid_mapping),
                                           _ptr(grid.block_offsets), _ptr(grid.tile_order), nb, grid.block_m,
                                           stream)
@@ -212,7 +225,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         nbytes = workspace_size(b, b if ft else rows_q, bm)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     st = lib.vlp_varlen_attn_fwd(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b, rows_q,
-                                 total_k, heads, head_dim, int(max_seqlen), float(scale), int(bool(causal)), ft,
+                                 total_k, heads, head_dim, q_st, k_st, o_st, int(max_seqlen), float(scale),
+                                 int(bool(causal)), ft,
                                  _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()), stream)
     _lib.check(st, "varlen_attn_fwd")
     return out, lse
@@ -259,9 +273,12 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         raise ValueError("q/out/dout [rows, H, D] and k, v [T, H, D] with matching H, D")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]):
         raise ValueError("lse must be float32 [H, rows]")
-    for t in (q, k, v, out, dout, lse):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    q_st, k_st, v_st = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    o_st, do_st = _token_stride(out, "out"), _token_stride(dout, "dout")
+    if k_st != v_st and k.shape[0] > 1:
+        raise ValueError("k and v must share one token stride")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     rows_q, heads, head_dim = (int(x) for x in q.shape)
@@ -269,9 +286,13 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     b = int(cu_seqlens_k.numel()) - 1
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(head_dim)))
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    dq_st, dk_st, dv_st = _token_stride(dq, "dq"), _token_stride(dk, "dk"), _token_stride(dv, "dv")
+    if dk_st != dv_st and dk.shape[0] > 1:
+        raise ValueError("dk and dv must share one token stride")
+    strides = (q_st, k_st, o_st, do_st, dq_st, dk_st)
     code = _DTYPE_CODES[q.dtype]
     if grids is not None:
         gq, gk = grids
@@ -282,7 +303,8 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
             return g.num_blocks if g.num_blocks is not None else int(g.grid_mapping.numel())
         st = lib.vlp_varlen_attn_bwd_grid(code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                           _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, rows_q, total_k, heads,
-                                          head_dim, int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq),
+                                          head_dim, *strides, int(max_seqlen), float(scale), int(bool(causal)),
+                                          _ptr(dq),
                                           _ptr(dk), _ptr(dv), _ptr(gq.grid_mapping), _ptr(gq.block_offsets),
                                           _ptr(gq.tile_order), nblocks(gq), _ptr(gk.grid_mapping),
                                           _ptr(gk.block_offsets), _ptr(gk.tile_order), nblocks(gk), gq.block_m,
@@ -297,7 +319,8 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     st = lib.vlp_varlen_attn_bwd(code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim,
-                                 int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 *strides, int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
+                                 _ptr(dv),
                                  _ptr(workspace), int(workspace.numel()), _stream_handle(q.device))
     _lib.check(st, "varlen_attn_bwd")
     return dq, dk, dv

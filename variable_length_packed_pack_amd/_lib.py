@@ -47,21 +47,25 @@ SIGNATURES = {
     "vlp_varlen_attn_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp]),
     "vlp_varlen_attn_fwd": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             *[ctypes.c_int64] * 3,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                              _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "vlp_varlen_attn_fwd_grid": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                  *[ctypes.c_int64] * 3,
                                                   ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                                   _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp]),
     "vlp_varlen_attn_bwd_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                                            ctypes.c_int32, ctypes.c_int32, _vp]),
     "vlp_varlen_attn_bwd": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                             ctypes.c_int32, *[ctypes.c_int64] * 6,
+                                             ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "vlp_varlen_attn_bwd_grid": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                                  ctypes.c_int32, *[ctypes.c_int64] * 6,
+                                                  ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp, _vp,
                                                   ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),

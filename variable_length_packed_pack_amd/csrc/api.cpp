@@ -45,13 +45,31 @@ GridWorkspace grid_workspace(int32_t num_seqs, int64_t cap) {
 struct Checked {
   int32_t block_m;
   int64_t grid_rows;  // rows the grid is sized for
+  int32_t q_stride, kv_stride, o_stride;  // resolved token strides (elements)
 };
 
-// Shared validation of the forward arguments; fills the tile size.
+inline int32_t element_bytes(int32_t dtype) { return dtype == VLP_FP32 ? 4 : 2; }
+
+// Token stride (elements between consecutive tokens) of a [rows, heads,
+// head_dim] operand whose heads are head_dim apart: 0 means contiguous.
+// Rows must start 16-byte aligned (the kernels move 16-byte chunks), and a
+// 64-row block must stay addressable with 32-bit byte offsets.
+vlp_status resolve_stride(int64_t stride, int32_t heads, int32_t head_dim, int32_t elt, int32_t* out) {
+  const int64_t row = static_cast<int64_t>(heads) * head_dim;
+  if (stride == 0) stride = row;
+  if (stride < row || (stride * elt) % 16 != 0) return VLP_ERR_INVALID;
+  if (stride * elt > (int64_t{1} << 24)) return VLP_ERR_OVERFLOW;
+  *out = static_cast<int32_t>(stride);
+  return VLP_OK;
+}
+
+// Shared validation of the forward arguments; fills the tile size and the
+// resolved strides.
 vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void* v,
                          const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs, int64_t rows_q,
-                         int64_t total_k, int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale,
-                         int32_t causal, int32_t first_token, const void* out, Checked* c) {
+                         int64_t total_k, int32_t heads, int32_t head_dim, int64_t q_stride, int64_t kv_stride,
+                         int64_t out_stride, int32_t max_seqlen, float scale, int32_t causal, int32_t first_token,
+                         const void* out, Checked* c) {
   if (!q || !k || !v || !out || !cu_k) return VLP_ERR_NULL;
   if (!first_token && !cu_q) return VLP_ERR_NULL;
   if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
@@ -66,7 +84,11 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
   c->block_m = vlp_kernel_block_m(dtype, head_dim, causal, first_token, num_seqs, rows_q, max_seqlen);
   if (c->block_m < 1) return VLP_ERR_UNSUPPORTED;
   c->grid_rows = first_token ? num_seqs : rows_q;
-  return VLP_OK;
+  const int32_t elt = element_bytes(dtype);
+  vlp_status st = resolve_stride(q_stride, heads, head_dim, elt, &c->q_stride);
+  if (st == VLP_OK) st = resolve_stride(kv_stride, heads, head_dim, elt, &c->kv_stride);
+  if (st == VLP_OK) st = resolve_stride(out_stride, heads, head_dim, elt, &c->o_stride);
+  return st;
 }
 
 // Factor taking raw scores to exp2 units.  Masked scores are -inf and must
@@ -76,8 +98,12 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
 float exp2_factor(float scale) { return scale > 0.0f ? scale * 1.4426950408889634f : 1.17549435e-38f; }
 
 vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-                        int32_t num_seqs, int64_t rows_q, int32_t heads, float scale, void* out, float* lse) {
+                        int32_t num_seqs, int64_t rows_q, int32_t heads, float scale, void* out, float* lse,
+                        const Checked& c) {
   vlp::AttnArgs a{};
+  a.q_stride = c.q_stride;
+  a.kv_stride = c.kv_stride;
+  a.o_stride = c.o_stride;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -181,12 +207,14 @@ extern "C" vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, in
 extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                           int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
-                                          int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                          int64_t out_row_stride, int32_t max_seqlen, float scale, int32_t causal,
                                           int32_t query_is_first_token, void* out, float* lse, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   Checked c{};
   vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
-                                head_dim, max_seqlen, scale, causal, query_is_first_token, out, &c);
+                                head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
+                                query_is_first_token, out, &c);
   if (st != VLP_OK) return st;
   if (!workspace) return VLP_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
@@ -205,7 +233,7 @@ extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const vo
   st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, s));
   if (st != VLP_OK) return st;
 
-  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse);
+  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse, c);
   a.grid_mapping = gm;
   a.block_offsets = bo;
   a.tile_order = to;
@@ -216,19 +244,21 @@ extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const vo
 extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k, const void* v,
                                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                                int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
-                                               int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
-                                               int32_t query_is_first_token, void* out, float* lse,
+                                               int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                               int64_t out_row_stride, int32_t max_seqlen, float scale,
+                                               int32_t causal, int32_t query_is_first_token, void* out, float* lse,
                                                const int32_t* grid_mapping, const int32_t* block_offsets,
                                                const int32_t* tile_order, int64_t num_blocks, int32_t block_m,
                                                void* stream) {
   Checked c{};
   vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
-                                head_dim, max_seqlen, scale, causal, query_is_first_token, out, &c);
+                                head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
+                                query_is_first_token, out, &c);
   if (st != VLP_OK) return st;
   if (!grid_mapping || !block_offsets) return VLP_ERR_NULL;
   if (num_blocks < 0 || block_m != c.block_m) return VLP_ERR_INVALID;
   if (num_blocks > INT32_MAX || num_blocks * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
-  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse);
+  vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse, c);
   a.grid_mapping = grid_mapping;
   a.block_offsets = block_offsets;
   a.tile_order = tile_order;
@@ -264,27 +294,43 @@ namespace {
 
 // Shared validation of the backward arguments (the forward's plus the
 // gradient buffers).
+struct BwdStrides {
+  int64_t q, kv, out, dout, dq, dkv;  // as passed (0 = contiguous)
+};
+
 vlp_status check_backward(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
                           const void* dout, const float* lse, const int32_t* cu_q, const int32_t* cu_k,
                           int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads, int32_t head_dim,
-                          int32_t max_seqlen, float scale, int32_t causal, const void* dq, const void* dk,
-                          const void* dv, Checked* c) {
-  vlp_status st = check_forward(dtype, q, k, v, cu_q, cu_k, num_seqs, rows_q, total_k, heads, head_dim, max_seqlen,
-                                scale, causal, 0, out, c);
+                          const BwdStrides& sd, int32_t max_seqlen, float scale, int32_t causal, const void* dq,
+                          const void* dk, const void* dv, Checked* c, int32_t* do_stride, int32_t* dq_stride,
+                          int32_t* dkv_stride) {
+  vlp_status st = check_forward(dtype, q, k, v, cu_q, cu_k, num_seqs, rows_q, total_k, heads, head_dim, sd.q, sd.kv,
+                                sd.out, max_seqlen, scale, causal, 0, out, c);
   if (st != VLP_OK) return st;
   if (!dout || !lse || !dq || !dk || !dv) return VLP_ERR_NULL;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return VLP_ERR_INVALID;
   if (rows_q * heads > INT32_MAX || total_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
-  return VLP_OK;
+  const int32_t elt = element_bytes(dtype);
+  st = resolve_stride(sd.dout, heads, head_dim, elt, do_stride);
+  if (st == VLP_OK) st = resolve_stride(sd.dq, heads, head_dim, elt, dq_stride);
+  if (st == VLP_OK) st = resolve_stride(sd.dkv, heads, head_dim, elt, dkv_stride);
+  return st;
 }
 
 vlp::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
                            const float* lse, const int32_t* cu_q, const int32_t* cu_k, int32_t num_seqs,
                            int64_t rows_q, int32_t heads, float scale, void* dq, void* dk, void* dv,
-                           float* row_stats) {
+                           float* row_stats, const Checked& c, int32_t do_stride, int32_t dq_stride,
+                           int32_t dkv_stride) {
   vlp::BwdArgs a{};
+  a.q_stride = c.q_stride;
+  a.kv_stride = c.kv_stride;
+  a.o_stride = c.o_stride;
+  a.do_stride = do_stride;
+  a.dq_stride = dq_stride;
+  a.dkv_stride = dkv_stride;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -312,12 +358,17 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
                                           const void* out, const void* dout, const float* lse,
                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                           int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
-                                          int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal,
+                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                          int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
+                                          int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal,
                                           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                           void* stream) {
   Checked c{};
+  int32_t do_stride = 0, dq_stride = 0, dkv_stride = 0;
+  const BwdStrides sd{q_row_stride, kv_row_stride, out_row_stride, dout_row_stride, dq_row_stride, dkv_row_stride};
   vlp_status st = check_backward(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q,
-                                 total_k, heads, head_dim, max_seqlen, scale, causal, dq, dk, dv, &c);
+                                 total_k, heads, head_dim, sd, max_seqlen, scale, causal, dq, dk, dv, &c, &do_stride,
+                                 &dq_stride, &dkv_stride);
   if (st != VLP_OK) return st;
   if (!workspace) return VLP_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
@@ -328,7 +379,8 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
   char* base = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
-                                 scale, dq, dk, dv, reinterpret_cast<float*>(base + w.off_lse2));
+                                 scale, dq, dk, dv, reinterpret_cast<float*>(base + w.off_lse2), c, do_stride,
+                                 dq_stride, dkv_stride);
   a.delta = reinterpret_cast<float*>(base + w.off_delta);
 
   // dQ over the query grid first: it also writes lse2 and delta, which the
@@ -366,14 +418,19 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
 extern "C" vlp_status vlp_varlen_attn_bwd_grid(
     int32_t dtype, const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
-    int32_t heads, int32_t head_dim, int32_t max_seqlen, float scale, int32_t causal, void* dq, void* dk, void* dv,
+    int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride, int64_t out_row_stride,
+    int64_t dout_row_stride, int64_t dq_row_stride, int64_t dkv_row_stride, int32_t max_seqlen, float scale,
+    int32_t causal, void* dq, void* dk, void* dv,
     const int32_t* q_grid_mapping, const int32_t* q_block_offsets, const int32_t* q_tile_order,
     int64_t q_num_blocks, const int32_t* k_grid_mapping, const int32_t* k_block_offsets,
     const int32_t* k_tile_order, int64_t k_num_blocks, int32_t block_m, float* row_stats, int32_t phases,
     void* stream) {
   Checked c{};
+  int32_t do_stride = 0, dq_stride = 0, dkv_stride = 0;
+  const BwdStrides sd{q_row_stride, kv_row_stride, out_row_stride, dout_row_stride, dq_row_stride, dkv_row_stride};
   vlp_status st = check_backward(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q,
-                                 total_k, heads, head_dim, max_seqlen, scale, causal, dq, dk, dv, &c);
+                                 total_k, heads, head_dim, sd, max_seqlen, scale, causal, dq, dk, dv, &c, &do_stride,
+                                 &dq_stride, &dkv_stride);
   if (st != VLP_OK) return st;
   if (phases < 1 || phases > 3) return VLP_ERR_INVALID;
   const bool run_dq = (phases & VLP_BWD_DQ) != 0, run_dkdv = (phases & VLP_BWD_DKDV) != 0;
@@ -386,7 +443,7 @@ extern "C" vlp_status vlp_varlen_attn_bwd_grid(
     return VLP_ERR_OVERFLOW;
   hipStream_t s = static_cast<hipStream_t>(stream);
   vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
-                                 scale, dq, dk, dv, row_stats);
+                                 scale, dq, dk, dv, row_stats, c, do_stride, dq_stride, dkv_stride);
   if (run_dq) {
     a.grid_mapping = q_grid_mapping;
     a.block_offsets = q_block_offsets;

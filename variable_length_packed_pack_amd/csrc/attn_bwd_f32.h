@@ -132,7 +132,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 4;
+  const int rs_bytes = a.kv_stride * 4;  // k / v tiles
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -144,13 +144,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
 
   // Resident half rows of Q and dO; delta from the forward output row.
   const int qrow = min(my_row, tc.lq - 1);
-  const size_t qidx = (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D;
+  const size_t qrow_g = static_cast<size_t>(tc.q_start + qrow), hoff = static_cast<size_t>(tc.head) * D;
   f32x4_t qv[HALF / 4], dov[HALF / 4];
   float delta;
   {
-    const float* qp = static_cast<const float*>(a.q) + qidx + hh * HALF;
-    const float* dop = static_cast<const float*>(a.dout) + qidx + hh * HALF;
-    const float* op = static_cast<const float*>(a.out) + qidx + hh * HALF;
+    const float* qp = static_cast<const float*>(a.q) + qrow_g * a.q_stride + hoff + hh * HALF;
+    const float* dop = static_cast<const float*>(a.dout) + qrow_g * a.do_stride + hoff + hh * HALF;
+    const float* op = static_cast<const float*>(a.out) + qrow_g * a.o_stride + hoff + hh * HALF;
     float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < HALF / 4; ++j) {
@@ -182,8 +182,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.0f;
 
-  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
-  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
+  const size_t kv_off = (static_cast<size_t>(tc.k_start) * a.kv_stride + static_cast<size_t>(tc.head) * D) * 4;
+  const char* kseq = static_cast<const char*>(a.k) + kv_off;
+  const char* vseq = static_cast<const char*>(a.v) + kv_off;
 
   auto issue_block = [&](int kb, char* buf) {
     const int nrows = min(BN, tc.lk - kb);
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   }
 
   if (!row_ok) return;
-  store_row_t_f32<D, DT32>(static_cast<float*>(a.dq) + qidx, acc, a.scale, hh);
+  store_row_t_f32<D, DT32>(static_cast<float*>(a.dq) + qrow_g * a.dq_stride + hoff, acc, a.scale, hh);
 }
 
 // ---------------------------------------------------------------------------
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   const int my_key = wk0 + n;
   const bool key_ok = my_key < tc.lk;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 4;
+  const int rs_q = a.q_stride * 4, rs_do = a.do_stride * 4;  // q / dout tiles
 
   const int q_begin = CAUSAL ? max(0, key0 - diag) : 0;
   const int nblocks = tc.lq > q_begin ? (tc.lq - q_begin + BQ - 1) / BQ : 0;
@@ -285,7 +286,8 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
 
   // Resident half rows of K and V.
   const int krow = min(my_key, tc.lk - 1);
-  const size_t kidx = (static_cast<size_t>(tc.k_start + krow) * a.heads + tc.head) * D;
+  const size_t krow_g = static_cast<size_t>(tc.k_start + krow), hoff = static_cast<size_t>(tc.head) * D;
+  const size_t kidx = krow_g * a.kv_stride + hoff;
   f32x4_t kv[HALF / 4], vv[HALF / 4];
   {
     const float* kp = static_cast<const float*>(a.k) + kidx + hh * HALF;
@@ -297,8 +299,9 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
     }
   }
 
-  int voff[LPW];
-  load_offsets_f32<D, LPW, RPI, CPR>(wave, lane, rs_bytes, voff);
+  int voff[LPW], voff_do[LPW];
+  load_offsets_f32<D, LPW, RPI, CPR>(wave, lane, rs_q, voff);
+  load_offsets_f32<D, LPW, RPI, CPR>(wave, lane, rs_do, voff_do);
   int qoff[HALF / 4];
 #pragma unroll
   for (int j = 0; j < HALF / 4; ++j) qoff[j] = n * RB + (((hh * (HALF / 4) + j) ^ chunk_swz_f32<D>(n)) << 4);
@@ -312,23 +315,23 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
       dv[d][r] = 0.0f;
     }
 
-  const size_t qseq_off = (static_cast<size_t>(tc.q_start) * a.heads + tc.head) * (D * 4);
-  const char* qseq = static_cast<const char*>(a.q) + qseq_off;
-  const char* doseq = static_cast<const char*>(a.dout) + qseq_off;
+  const char* qseq = static_cast<const char*>(a.q) + (static_cast<size_t>(tc.q_start) * a.q_stride + hoff) * 4;
+  const char* doseq = static_cast<const char*>(a.dout) + (static_cast<size_t>(tc.q_start) * a.do_stride + hoff) * 4;
   const size_t stat0 = static_cast<size_t>(tc.head) * a.rows_q + tc.q_start;
 
   auto issue_block = [&](int qb, char* buf) {
     const int nrows = min(BQ, tc.lq - qb);
-    const int nrec = (nrows - 1) * rs_bytes + RB;
-    const size_t boff = static_cast<size_t>(qb) * rs_bytes;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(qseq + boff), 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(doseq + boff), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(qseq + static_cast<size_t>(qb) * rs_q), 0, (nrows - 1) * rs_q + RB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(doseq + static_cast<size_t>(qb) * rs_do), 0, (nrows - 1) * rs_do + RB, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
-      const int vo = voff[i];  // (a local copy: passing voff[i] directly drops the host-side kernel stub)
+      const int vo = voff[i];  // (local copies: passing voff[i] directly drops the host-side kernel stub)
+      const int vd = voff_do[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vd, 0, 0, 0);
     }
     if (wave == 0) {
       // 64 lanes x 4 bytes: the block's lse2 and delta (zeros past the end).
@@ -400,8 +403,9 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   }
 
   if (!key_ok) return;
-  store_row_t_f32<D, DT32>(static_cast<float*>(a.dk) + kidx, dk, a.scale, hh);
-  store_row_t_f32<D, DT32>(static_cast<float*>(a.dv) + kidx, dv, 1.0f, hh);
+  const size_t dkidx = krow_g * a.dkv_stride + hoff;
+  store_row_t_f32<D, DT32>(static_cast<float*>(a.dk) + dkidx, dk, a.scale, hh);
+  store_row_t_f32<D, DT32>(static_cast<float*>(a.dv) + dkidx, dv, 1.0f, hh);
 }
 
 }  // namespace vlp

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 2;
+  const int rs_bytes = a.kv_stride * 2;  // k / v tiles
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -259,13 +259,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   // Resident rows: Q and dO of this lane's query (rows past the sequence end
   // repeat the last real row; their results are never stored).
   const int qrow = min(my_row, tc.lq - 1);
-  const size_t qidx = (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D;
+  const size_t qrow_g = static_cast<size_t>(tc.q_start + qrow), hoff = static_cast<size_t>(tc.head) * D;
   u32x4_t qv[KS], dov[KS];
   float delta;
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qidx;
-    const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qidx;
-    const uint16_t* op = static_cast<const uint16_t*>(a.out) + qidx;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow_g * a.q_stride + hoff;
+    const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qrow_g * a.do_stride + hoff;
+    const uint16_t* op = static_cast<const uint16_t*>(a.out) + qrow_g * a.o_stride + hoff;
     float part = 0.0f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -301,8 +301,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.0f;
 
-  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
-  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
+  const size_t kv_off = (static_cast<size_t>(tc.k_start) * a.kv_stride + static_cast<size_t>(tc.head) * D) * 2;
+  const char* kseq = static_cast<const char*>(a.k) + kv_off;
+  const char* vseq = static_cast<const char*>(a.v) + kv_off;
 
   auto issue_block = [&](int kb, char* buf) {
     const int nrows = min(BN, tc.lk - kb);
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   }
 
   if (!row_ok) return;
-  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dq) + qidx, acc, a.scale, hh);
+  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dq) + qrow_g * a.dq_stride + hoff, acc, a.scale, hh);
 }
 
 // ---------------------------------------------------------------------------
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   const int my_key = wk0 + n;
   const bool key_ok = my_key < tc.lk;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 2;
+  const int rs_q = a.q_stride * 2, rs_do = a.do_stride * 2;  // q / dout tiles
 
   // Queries that see some key of this tile: p + diag >= key0 when causal.
   const int q_begin = CAUSAL ? max(0, key0 - diag) : 0;
@@ -405,7 +406,8 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
 
   // Resident rows: K and V of this lane's key.
   const int krow = min(my_key, tc.lk - 1);
-  const size_t kidx = (static_cast<size_t>(tc.k_start + krow) * a.heads + tc.head) * D;
+  const size_t krow_g = static_cast<size_t>(tc.k_start + krow), hoff = static_cast<size_t>(tc.head) * D;
+  const size_t kidx = krow_g * a.kv_stride + hoff;
   u32x4_t kv[KS], vv[KS];
   {
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + kidx;
@@ -417,8 +419,9 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
     }
   }
 
-  int voff[LPW];
-  load_offsets<D, LPW, RPI, CPR>(wave, lane, rs_bytes, voff);
+  int voff[LPW], voff_do[LPW];
+  load_offsets<D, LPW, RPI, CPR>(wave, lane, rs_q, voff);
+  load_offsets<D, LPW, RPI, CPR>(wave, lane, rs_do, voff_do);
   int yoff[KS], ytoff[2][DT32];
   tile_offsets<D, KS, DT32, RB>(lane, yoff, ytoff);
 
@@ -431,23 +434,23 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
       dv[d][r] = 0.0f;
     }
 
-  const size_t qseq_off = (static_cast<size_t>(tc.q_start) * a.heads + tc.head) * (D * 2);
-  const char* qseq = static_cast<const char*>(a.q) + qseq_off;
-  const char* doseq = static_cast<const char*>(a.dout) + qseq_off;
+  const char* qseq = static_cast<const char*>(a.q) + (static_cast<size_t>(tc.q_start) * a.q_stride + hoff) * 2;
+  const char* doseq = static_cast<const char*>(a.dout) + (static_cast<size_t>(tc.q_start) * a.do_stride + hoff) * 2;
   const size_t stat0 = static_cast<size_t>(tc.head) * a.rows_q + tc.q_start;
 
   auto issue_block = [&](int qb, char* buf) {
     const int nrows = min(BQ, tc.lq - qb);
-    const int nrec = (nrows - 1) * rs_bytes + RB;
-    const size_t boff = static_cast<size_t>(qb) * rs_bytes;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(qseq + boff), 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(doseq + boff), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(qseq + static_cast<size_t>(qb) * rs_q), 0, (nrows - 1) * rs_q + RB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(doseq + static_cast<size_t>(qb) * rs_do), 0, (nrows - 1) * rs_do + RB, 0x00020000);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
-      const int vo = voff[i];  // (a local copy: passing voff[i] directly drops the host-side kernel stub)
+      const int vo = voff[i];  // (local copies: passing voff[i] directly drops the host-side kernel stub)
+      const int vd = voff_do[i];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vd, 0, 0, 0);
     }
     if (wave == 0) {
       // 64 lanes x 4 bytes per load: the block's lse2 and delta (zeros past
@@ -521,8 +524,9 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   }
 
   if (!key_ok) return;
-  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dk) + kidx, dk, a.scale, hh);
-  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dv) + kidx, dv, 1.0f, hh);
+  const size_t dkidx = krow_g * a.dkv_stride + hoff;
+  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dk) + dkidx, dk, a.scale, hh);
+  store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dv) + dkidx, dv, 1.0f, hh);
 }
 
 }  // namespace vlp

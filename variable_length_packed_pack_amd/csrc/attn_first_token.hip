@@ -126,19 +126,18 @@ __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a,
 
   const int grp = lane / LPK;   // key slot within a step
   const int c = lane % LPK;     // chunk of the row
-  const size_t rs = static_cast<size_t>(a.heads) * D;
 
   float qf[EPC];
   {
     const char* qp = static_cast<const char*>(a.q) +
-                     ((static_cast<size_t>(seq) * a.heads + head) * D + c * EPC) * (16 / EPC);
+                     (static_cast<size_t>(seq) * a.q_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
     C::widen(*reinterpret_cast<const u32x4_t*>(qp), qf);
   }
-  const char* kp = static_cast<const char*>(a.k) +
-                   ((static_cast<size_t>(k_start) * a.heads + head) * D + c * EPC) * (16 / EPC);
-  const char* vp = static_cast<const char*>(a.v) +
-                   ((static_cast<size_t>(k_start) * a.heads + head) * D + c * EPC) * (16 / EPC);
-  const size_t row_bytes = rs * (16 / EPC);
+  const size_t kv_off =
+      (static_cast<size_t>(k_start) * a.kv_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
+  const char* kp = static_cast<const char*>(a.k) + kv_off;
+  const char* vp = static_cast<const char*>(a.v) + kv_off;
+  const size_t row_bytes = static_cast<size_t>(a.kv_stride) * (16 / EPC);
 
   float m = kNegInf, l = 0.0f, acc[EPC];
 #pragma unroll
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a,
 #pragma unroll
     for (int e = 0; e < EPC; ++e) o[e] = acc[e] * inv;
     char* op = static_cast<char*>(a.out) +
-               ((static_cast<size_t>(seq) * a.heads + head) * D + c * EPC) * (16 / EPC);
+               (static_cast<size_t>(seq) * a.o_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
     *reinterpret_cast<u32x4_t*>(op) = C::narrow(o);
     if (c == 0 && a.lse)
       a.lse[static_cast<size_t>(head) * a.rows_q + seq] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 2;  // bytes between consecutive tokens of one head
+  const int rs_bytes = a.kv_stride * 2;  // bytes between consecutive tokens of one head of k / v
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -291,8 +291,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   u32x4_t qv[KS];
   {
     const int qrow = min(my_row, tc.lq - 1);
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(tc.q_start + qrow) * a.q_stride +
+                         static_cast<size_t>(tc.head) * D;
 #pragma unroll
     for (int k = 0; k < KS; ++k) qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
   }
@@ -340,8 +340,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   float m = kNegInf;
   float l = 0.0f;
 
-  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
-  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 2);
+  const size_t kv_off = (static_cast<size_t>(tc.k_start) * a.kv_stride + static_cast<size_t>(tc.head) * D) * 2;
+  const char* kseq = static_cast<const char*>(a.k) + kv_off;
+  const char* vseq = static_cast<const char*>(a.v) + kv_off;
 
   // Stream key block [kb, kb + BN) of K and V into one LDS buffer.
   auto issue_block = [&](int kb, char* buf) {
@@ -436,8 +437,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   const float l_tot = l + __shfl_xor(l, 32);
   if (!row_ok) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  uint16_t* op = static_cast<uint16_t*>(a.out) +
-                 (static_cast<size_t>(tc.q_start + my_row) * a.heads + tc.head) * D;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + static_cast<size_t>(tc.q_start + my_row) * a.o_stride +
+                 static_cast<size_t>(tc.head) * D;
 #pragma unroll
   for (int d = 0; d < DT32; ++d)
 #pragma unroll
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < tc.lq;
   const int diag = tc.lk - tc.lq;
-  const int rs_bytes = a.heads * D * 4;
+  const int rs_bytes = a.kv_stride * 4;
 
   int kv_end = tc.lk;
   if (CAUSAL) kv_end = min(tc.lk, row0 + tile_rows + diag);
@@ -525,8 +526,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   f32x4_t qv[HALF / 4];
   {
     const int qrow = min(my_row, tc.lq - 1);
-    const float* qp = static_cast<const float*>(a.q) +
-                      (static_cast<size_t>(tc.q_start + qrow) * a.heads + tc.head) * D + hh * HALF;
+    const float* qp = static_cast<const float*>(a.q) + static_cast<size_t>(tc.q_start + qrow) * a.q_stride +
+                      static_cast<size_t>(tc.head) * D + hh * HALF;
 #pragma unroll
     for (int j = 0; j < HALF / 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(qp + 4 * j);
   }
@@ -556,8 +557,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   float m = kNegInf;
   float l = 0.0f;
 
-  const char* kseq = static_cast<const char*>(a.k) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
-  const char* vseq = static_cast<const char*>(a.v) + (static_cast<size_t>(tc.k_start) * a.heads + tc.head) * (D * 4);
+  const size_t kv_off = (static_cast<size_t>(tc.k_start) * a.kv_stride + static_cast<size_t>(tc.head) * D) * 4;
+  const char* kseq = static_cast<const char*>(a.k) + kv_off;
+  const char* vseq = static_cast<const char*>(a.v) + kv_off;
 
   auto issue_block = [&](int kb, char* buf) {
     const int nrows = min(BN, tc.lk - kb);
@@ -633,7 +635,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   const float l_tot = l + __shfl_xor(l, 32);
   if (!row_ok) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  float* op = static_cast<float*>(a.out) + (static_cast<size_t>(tc.q_start + my_row) * a.heads + tc.head) * D;
+  float* op = static_cast<float*>(a.out) + static_cast<size_t>(tc.q_start + my_row) * a.o_stride +
+              static_cast<size_t>(tc.head) * D;
 #pragma unroll
   for (int d = 0; d < DT32; ++d)
 #pragma unroll

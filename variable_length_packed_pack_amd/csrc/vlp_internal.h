@@ -31,6 +31,12 @@ struct AttnArgs {
   int32_t num_blocks;          // G when known on the host, -1: read block_offsets[num_seqs]
   int32_t grid_cap;            // entries of grid_mapping / tile_order (guards bad metadata)
   float scale_log2;            // scale * log2(e): scores go straight to exp2
+  // Elements between consecutive tokens (a head's D elements are contiguous
+  // and heads are D apart): heads * head_dim for contiguous tensors, more for
+  // views into a fused projection output.
+  int32_t q_stride;
+  int32_t kv_stride;           // k and v
+  int32_t o_stride;
 };
 
 // Arguments of the two backward launches (the dQ kernel over the query
@@ -58,6 +64,13 @@ struct BwdArgs {
   int32_t grid_cap;
   float scale;                 // factor of dq and dk
   float scale_log2;            // scores -> exp2 units
+  // Elements between consecutive tokens, as in AttnArgs.
+  int32_t q_stride;
+  int32_t kv_stride;           // k and v
+  int32_t o_stride;            // out
+  int32_t do_stride;           // dout
+  int32_t dq_stride;
+  int32_t dkv_stride;          // dk and dv
 };
 
 // Kernel families and their tile shapes.  block_m is the query rows per
