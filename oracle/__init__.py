@@ -20,6 +20,10 @@ definition from the pages:
                              per sequence); "gigl.nn.packed_attention" (each
                              sequence attends only to itself; first-token
                              queries).
+* ``ragged_matmul``       -- "PyCoRa", "Ragged Matrix Multiplication" (each
+                             sequence times its own weight matrix); a shared
+                             weight gives the packed projections of
+                             "gigl.nn.packed_attention".
 * ``varlen_attention_bwd`` -- the gradient of ``varlen_attention`` (no first-
                              token mode) with respect to q, k and v; the pages
                              train through the packed attention
@@ -36,6 +40,7 @@ from .varlen_oracle import (  # noqa: F401
     decode_tile,
     grid_capacity,
     pack_sequences,
+    ragged_matmul,
     varlen_attention,
     varlen_attention_bwd,
     varlen_attention_bwd_rows,

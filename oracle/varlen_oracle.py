@@ -404,3 +404,36 @@ def varlen_attention_bwd_rows(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, scale: 
     d = q.shape[2]
     return (np.asarray(dqs).reshape(-1, d), np.asarray(dks).reshape(-1, d),
             np.asarray(dvs).reshape(-1, d))
+
+
+# ---------------------------------------------------------------------------
+# Ragged matrix multiplication ("PyCoRa", "Ragged Matrix Multiplication":
+# each sequence of the packed batch is multiplied by its own weight matrix;
+# with one weight shared by all sequences this is the packed projection of
+# "gigl.nn.packed_attention", "Why this exists": linear layers on the
+# [num_tokens, dim] buffer)
+# ---------------------------------------------------------------------------
+
+def ragged_matmul(x, weight, cu_seqlens, bias=None, shared_weight=False, shared_bias=False):
+    """y[rows of sequence i] = x[rows of sequence i] @ weight_i^T + bias_i.
+
+    x [rows, K]; weight [B, N, K] (one [N, K] matrix per sequence, the
+    layout of a linear layer's weight), or [N, K] when ``shared_weight``;
+    bias None, [B, N], or [N] when ``shared_bias``.  Returns y [rows, N] in
+    float64; rows owned by no sequence stay zero (the GPU never writes them).
+    """
+    x64 = _as_f64(x)
+    w64 = _as_f64(weight)
+    b64 = None if bias is None else _as_f64(bias)
+    cu = [int(c) for c in np.asarray(cu_seqlens).tolist()]
+    n_out = w64.shape[-2]
+    y = np.zeros((x64.shape[0], n_out))
+    for i in range(len(cu) - 1):
+        r0, r1 = cu[i], cu[i + 1]
+        if r1 == r0:
+            continue
+        w = w64 if shared_weight else w64[i]
+        y[r0:r1] = x64[r0:r1] @ w.T
+        if b64 is not None:
+            y[r0:r1] += b64 if shared_bias else b64[i]
+    return y
