@@ -412,6 +412,121 @@ def bench_backward(args, wl, dev) -> int:
     return 0
 
 
+def bench_matmul(args, wl, dev) -> int:
+    """Ragged matrix multiplication on the workload's token split: the packed
+    QKV projection (hidden = heads x head_dim -> 3 x hidden, one shared
+    weight) or, with --matmul per-seq, one [hidden, hidden] weight per
+    sequence ("PyCoRa", "Ragged Matrix Multiplication")."""
+    import torch
+
+    import variable_length_packed_pack_amd as vlp
+
+    t, b = wl.total_tokens, wl.num_seqs
+    hidden = wl.heads * wl.head_dim
+    per_seq = args.matmul == "per-seq"
+    n_out = hidden if per_seq else 3 * hidden
+    g = torch.Generator(device="cpu").manual_seed(77)
+    tdt = torch.bfloat16
+    x = torch.randn(t, hidden, generator=g).to(tdt).to(dev)
+    wshape = (b, n_out, hidden) if per_seq else (n_out, hidden)
+    w = (torch.randn(*wshape, generator=g) / math.sqrt(hidden)).to(tdt).to(dev)
+    cu_host = torch.from_numpy(wl.cu_seqlens_host())
+    cu = cu_host.to(dev)
+    y = torch.empty(t, n_out, dtype=tdt, device=dev)
+    nb = vlp._lib.load()  # noqa: F841  (loads the library before timing)
+    ws_bytes = __import__("ctypes").c_size_t(0)
+    vlp._lib.check(vlp._lib.load().vlp_ragged_matmul_workspace_size(b, t, __import__("ctypes").addressof(ws_bytes)),
+                   "workspace")
+    ws = torch.empty(max(int(ws_bytes.value), 256), dtype=torch.uint8, device=dev)
+    flops = 2.0 * t * hidden * n_out
+    nbytes = 2.0 * (t * hidden + (b if per_seq else 1) * n_out * hidden + t * n_out)
+
+    def run():
+        vlp.ragged_matmul(x, w, cu, None, out=y, workspace=ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+    stream.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # library reference on the same packed rows (hipBLASLt through torch)
+    lib_ms = None
+    with torch.cuda.stream(stream):
+        if per_seq:
+            def ref():
+                for i in range(b):
+                    s0, e0 = int(cu_host[i]), int(cu_host[i + 1])
+                    torch.matmul(x[s0:e0], w[i].t(), out=y[s0:e0])
+        else:
+            def ref():
+                torch.matmul(x, w.t(), out=y)
+        for _ in range(3):
+            ref()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            ref()
+        ev1.record(stream)
+    stream.synchronize()
+    lib_ms = ev0.elapsed_time(ev1) / args.steps
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle  # test infrastructure: used only for this reported baseline
+        xs, ws_ = x.float().cpu(), w.float().cpu()
+        elapsed, done, fl = 0.0, 0, 0.0
+        order = np.argsort(-wl.lengths)[::-1]  # shortest sequences first, until the budget is spent
+        for i in order:
+            s0, e0 = int(cu_host[i]), int(cu_host[i + 1])
+            cu1 = np.array([0, e0 - s0], dtype=np.int32)
+            t0 = time.perf_counter()
+            oracle.ragged_matmul(xs[s0:e0], ws_[i:i + 1] if per_seq else ws_, cu1, shared_weight=not per_seq)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            fl += 2.0 * (e0 - s0) * hidden * n_out
+            if elapsed > args.cpu_budget:
+                break
+        cpu = {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle",
+               "sample": f"{done} of {b} sequences (shortest first), fp64 numpy, {fl / 1e9:.1f} GFLOP, {elapsed:.1f} s"}
+
+    achieved = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "ragged matmul TFLOP/s (% MFMA peak), 1 GPU",
+        "value": round(achieved, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset)",
+        "config": {"workload": wl.name + (" per-sequence weights" if per_seq else " shared QKV projection"),
+                   "rows": t, "num_seqs": b, "in_features": hidden, "out_features": n_out,
+                   "weights": b if per_seq else 1},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "library_gemm_ms": round(lib_ms, 4),
+        "library_gemm_tflops": round(flops / (lib_ms * 1e-3) / 1e12, 3),
+        "vs_library_gemm": round(lib_ms / ms, 3),
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "compulsory_gb": round(nbytes / 1e9, 4),
+        "note": "each timed call includes the device grid build (~10 us)",
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +541,8 @@ def main() -> int:
                     help="query_is_first_token mode: one query per sequence (its first token)")
     ap.add_argument("--backward", action="store_true",
                     help="measure the gradients (dq, dk, dv) instead of the forward")
+    ap.add_argument("--matmul", choices=["shared", "per-seq"], default=None,
+                    help="measure the ragged matrix multiplication on the workload's token split instead")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
                          "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -458,6 +575,8 @@ def main() -> int:
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)
+    if args.matmul:
+        return bench_matmul(args, wl, dev)
     if args.backward:
         if args.first_token:
             print("--backward has no first-token mode", file=sys.stderr)

@@ -381,6 +381,64 @@ vlp_status vlp_varlen_attn_bwd_grid(int32_t dtype, const void* q, const void* k,
                                     int64_t k_num_blocks, int32_t block_m, float* row_stats, int32_t phases,
                                     void* stream);
 
+/*
+ * Token rows per tile of the ragged grid that vlp_ragged_matmul walks.
+ */
+#define VLP_MATMUL_BLOCK_M 128
+
+/*
+ * vlp_ragged_matmul_workspace_size -- bytes of device workspace that
+ * vlp_ragged_matmul needs (its device-built grid: G_cap(rows, num_seqs,
+ * VLP_MATMUL_BLOCK_M) tiles).
+ * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows < 0 ->
+ * VLP_ERR_INVALID.
+ */
+vlp_status vlp_ragged_matmul_workspace_size(int32_t num_seqs, int64_t rows, size_t* bytes);
+
+/*
+ * vlp_ragged_matmul -- y = x W_i^T (+ b_i) on the rows of every sequence i
+ * of a packed batch.
+ *
+ * "PyCoRa", "Ragged Matrix Multiplication": each sequence is multiplied by
+ * its own weight matrix, thread blocks finding their sequence through the
+ * ragged-grid metadata ("CoRa Metadata").  With weight_seq_stride = 0 every
+ * sequence shares one weight: the packed linear layer of
+ * "gigl.nn.packed_attention" ("Why this exists").  Enqueues on `stream` the
+ * device grid build and one launch; no host read of cu_seqlens.
+ *
+ *   dtype          VLP_BF16 or VLP_FP16 (VLP_FP32 -> VLP_ERR_UNSUPPORTED);
+ *                  fp32 accumulation, y rounded to dtype once.
+ *   x              device [rows, in_features], contiguous.
+ *   weight         device; sequence i's matrix is [out_features,
+ *                  in_features] row-major (a linear layer's weight) at
+ *                  weight + i * weight_seq_stride elements.
+ *   bias           device or NULL; sequence i's bias is out_features
+ *                  elements at bias + i * bias_seq_stride.
+ *   cu_seqlens     device int32 [num_seqs + 1]: cu[0] = 0, non-decreasing,
+ *                  cu[B] <= rows; zero-length sequences allowed.
+ *   rows           physical rows of x and y; rows not owned by a sequence
+ *                  are never written.
+ *   in_features    a multiple of 64 in [64, 65536].
+ *   out_features   a multiple of 4 in [4, 65536].
+ *   weight_seq_stride, bias_seq_stride  >= 0; 0 = shared; multiples of 8
+ *                  (weight) and 4 (bias) elements.
+ *   y              device [rows, out_features], contiguous; must not overlap
+ *                  x, weight or bias.
+ *   workspace      device, >= vlp_ragged_matmul_workspace_size bytes,
+ *                  256-byte aligned; overwritten.
+ * x, weight, bias and y must be 16-byte aligned.
+ * Errors: NULL x/weight/cu_seqlens/y/workspace -> VLP_ERR_NULL; dtype not
+ * built -> VLP_ERR_UNSUPPORTED; num_seqs < 1, rows < 0, feature counts out of
+ * range or not multiples, negative or misaligned strides, misaligned pointers
+ * -> VLP_ERR_INVALID; rows beyond int32 or a grid beyond int32 workgroups ->
+ * VLP_ERR_OVERFLOW; small workspace -> VLP_ERR_CAPACITY; launch failure ->
+ * VLP_ERR_HIP.
+ */
+vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, const void* bias,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows, int32_t in_features,
+                             int32_t out_features, int64_t weight_seq_stride, int64_t bias_seq_stride, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* vlp_status_string -- a static, human-readable name for a status code; for
  * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */
 const char* vlp_status_string(vlp_status status);

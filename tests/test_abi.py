@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     for must in ("vlp_pack_sequences", "vlp_build_ragged_grid", "vlp_varlen_attn_fwd",
                  "vlp_varlen_attn_fwd_grid", "vlp_build_ragged_grid_device", "vlp_grid_capacity",
                  "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string",
-                 "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size"):
+                 "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size", "vlp_ragged_matmul"):
         assert must in names
 
 
@@ -51,6 +51,7 @@ def test_header_constants_match_binding():
     assert "#define VLP_FIRST_TOKEN_BLOCK_M (1 << 30)" in text
     assert f"#define VLP_BWD_DQ {_lib.VLP_BWD_DQ}" in text and f"#define VLP_BWD_DKDV {_lib.VLP_BWD_DKDV}" in text
     assert f"#define VLP_BWD_BLOCK_K {_lib.VLP_BWD_BLOCK_K}" in text
+    assert f"#define VLP_MATMUL_BLOCK_M {_lib.VLP_MATMUL_BLOCK_M}" in text
     for name in ("VLP_FP32 = 0", "VLP_FP16 = 1", "VLP_BF16 = 2", "VLP_OK = 0", "VLP_ERR_HIP = 6"):
         assert name in text
 
@@ -339,6 +340,34 @@ def test_backward_workspace_size():
     ck = vlp.grid_capacity(70000, 64, vlp.VLP_BWD_BLOCK_K)
     assert n.value >= 2 * 4 * 16 * 65536 + 4 * (2 * 65 + 2 * cq + 2 * ck)
     assert n.value == vlp.bwd_workspace_size(64, 65536, 70000, 16, 128)
+
+
+def _mm(**kw):
+    lib = _lib.load()
+    a = dict(dtype=2, x=FAKE, w=FAKE, bias=None, cu=FAKE, b=4, rows=100, k=512, n=256, ws_=0, bs=0, y=FAKE, ws=FAKE,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.vlp_ragged_matmul(a["dtype"], a["x"], a["w"], a["bias"], a["cu"], a["b"], a["rows"], a["k"], a["n"],
+                                 a["ws_"], a["bs"], a["y"], a["ws"], a["ws_bytes"], None)
+
+
+def test_ragged_matmul_validation_errors():
+    for name in ("x", "w", "cu", "y", "ws"):
+        assert _mm(**{name: None}) == 1, name
+    assert _mm(dtype=0) == 3 and _mm(dtype=9) == 3
+    assert _mm(b=0) == 2 and _mm(rows=-1) == 2
+    assert _mm(k=96) == 2 and _mm(k=0) == 2 and _mm(k=65600) == 2   # multiples of 64 up to 65536
+    assert _mm(n=6) == 2 and _mm(n=0) == 2
+    assert _mm(ws_=-8) == 2 and _mm(ws_=12) == 2
+    assert _mm(bias=FAKE, bs=2) == 2
+    assert _mm(x=FAKE + 8) == 2 and _mm(bias=FAKE + 4) == 2 and _mm(ws=FAKE + 64) == 2
+    assert _mm(rows=2**31) == 5
+    assert _mm(ws_bytes=8) == 4
+    lib = _lib.load()
+    nb = ctypes.c_size_t(0)
+    assert lib.vlp_ragged_matmul_workspace_size(64, 65536, ctypes.addressof(nb)) == 0
+    assert nb.value >= 4 * (65 + 2 * vlp.grid_capacity(65536, 64, vlp.VLP_MATMUL_BLOCK_M))
+    assert lib.vlp_ragged_matmul_workspace_size(0, 10, ctypes.addressof(nb)) == 2
 
 
 def test_device_grid_validation_errors():

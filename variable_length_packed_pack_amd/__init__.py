@@ -16,6 +16,9 @@ Functions mirror the pages' calls:
 * ``varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k,
   max_seqlen, scale, causal) -> (dq, dk, dv)``, the gradients of the same
   attention ("gigl.nn.packed_attention", "Why this exists").
+* ``ragged_matmul(x, weight, cu_seqlens, bias) -> y``: every sequence times its
+  own weight matrix, or one shared weight ("PyCoRa", "Ragged Matrix
+  Multiplication").
 """
 
 from __future__ import annotations
@@ -37,6 +40,7 @@ from ._lib import (  # noqa: F401
     VLP_FIRST_TOKEN_BLOCK_M,
     VLP_FP16,
     VLP_FP32,
+    VLP_MATMUL_BLOCK_M,
     VlpError,
 )
 
@@ -324,3 +328,58 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                                  _ptr(workspace), int(workspace.numel()), _stream_handle(q.device))
     _lib.check(st, "varlen_attn_bwd")
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# ragged matrix multiplication
+# ---------------------------------------------------------------------------
+
+def ragged_matmul(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, *,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x_i @ weight_i^T (+ bias_i) for the rows of every sequence i.
+
+    x [rows, K] contiguous; weight [B, N, K] (one linear-layer weight per
+    sequence) or [N, K] (shared); bias None, [B, N] or [N]; cu_seqlens int32
+    [B+1] on the device.  Returns y [rows, N]; rows owned by no sequence are
+    left as they were (fresh outputs come from ``torch.empty``).
+    """
+    lib = _lib.load()
+    if not (x.is_cuda and weight.is_cuda and cu_seqlens.is_cuda):
+        raise ValueError("x, weight and cu_seqlens must be device tensors")
+    if x.dtype not in _DTYPE_CODES or weight.dtype != x.dtype or (bias is not None and bias.dtype != x.dtype):
+        raise TypeError("x, weight and bias must share one of float16 / bfloat16")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    for t in (x, weight) + (() if bias is None else (bias,)):
+        if not t.is_contiguous():
+            raise ValueError("x, weight and bias must be contiguous")
+    b = int(cu_seqlens.numel()) - 1
+    rows, k = (int(d) for d in x.shape)
+    if weight.dim() == 2:
+        n, w_stride = int(weight.shape[0]), 0
+    elif weight.dim() == 3 and weight.shape[0] == b:
+        n, w_stride = int(weight.shape[1]), int(weight.shape[1] * weight.shape[2])
+    else:
+        raise ValueError("weight must be [N, K] or [num_seqs, N, K]")
+    if int(weight.shape[-1]) != k:
+        raise ValueError("weight's last dimension must equal x's")
+    b_stride = 0
+    if bias is not None:
+        if bias.dim() == 2 and bias.shape[0] == b and bias.shape[1] == n:
+            b_stride = n
+        elif not (bias.dim() == 1 and bias.shape[0] == n):
+            raise ValueError("bias must be [N] or [num_seqs, N]")
+    if out is None:
+        out = torch.empty(rows, n, dtype=x.dtype, device=x.device)
+    elif out.shape != (rows, n) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [rows, N] tensor of x's dtype")
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _lib.check(lib.vlp_ragged_matmul_workspace_size(b, rows, ctypes.addressof(nb)), "ragged_matmul")
+        workspace = torch.empty(max(int(nb.value), 256), dtype=torch.uint8, device=x.device)
+    st = lib.vlp_ragged_matmul(_DTYPE_CODES[x.dtype], _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), b, rows,
+                               k, n, w_stride, b_stride, _ptr(out), _ptr(workspace), int(workspace.numel()),
+                               _stream_handle(x.device))
+    _lib.check(st, "ragged_matmul")
+    return out

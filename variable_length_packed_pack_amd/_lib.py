@@ -29,6 +29,7 @@ VLP_DEVICE_SORT_MAX_SEQS = 4096
 VLP_BWD_DQ = 1
 VLP_BWD_DKDV = 2
 VLP_BWD_BLOCK_K = 64
+VLP_MATMUL_BLOCK_M = 128
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -68,6 +69,10 @@ SIGNATURES = {
                                                   ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp, _vp,
                                                   ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
+    "vlp_ragged_matmul_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int64, _vp]),
+    "vlp_ragged_matmul": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp,
+                                           _vp, ctypes.c_size_t, _vp]),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 

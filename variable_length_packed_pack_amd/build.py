@@ -44,6 +44,7 @@ SOURCES = [
     "attn_bwd_bf16.hip",
     "attn_bwd_f16.hip",
     "attn_bwd_f32.hip",
+    "ragged_matmul.hip",
 ]
 
 

@@ -461,3 +461,59 @@ extern "C" vlp_status vlp_varlen_attn_bwd_grid(
   }
   return st;
 }
+
+extern "C" vlp_status vlp_ragged_matmul_workspace_size(int32_t num_seqs, int64_t rows, size_t* bytes) {
+  if (!bytes) return VLP_ERR_NULL;
+  if (num_seqs < 1 || rows < 0) return VLP_ERR_INVALID;
+  *bytes = grid_workspace(num_seqs, vlp_grid_capacity(rows, num_seqs, VLP_MATMUL_BLOCK_M)).bytes;
+  return VLP_OK;
+}
+
+extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, const void* bias,
+                                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows,
+                                        int32_t in_features, int32_t out_features, int64_t weight_seq_stride,
+                                        int64_t bias_seq_stride, void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!x || !weight || !cu_seqlens || !y || !workspace) return VLP_ERR_NULL;
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
+  if (dtype == VLP_FP32) return VLP_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || rows < 0) return VLP_ERR_INVALID;
+  if (in_features < 64 || in_features > 65536 || in_features % 64 != 0) return VLP_ERR_INVALID;
+  if (out_features < 4 || out_features > 65536 || out_features % 4 != 0) return VLP_ERR_INVALID;
+  if (weight_seq_stride < 0 || weight_seq_stride % 8 != 0) return VLP_ERR_INVALID;
+  if (bias && (bias_seq_stride < 0 || bias_seq_stride % 4 != 0)) return VLP_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(y) || (bias && !aligned16(bias))) return VLP_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
+  if (rows > INT32_MAX) return VLP_ERR_OVERFLOW;
+  const int64_t cap = vlp_grid_capacity(rows, num_seqs, VLP_MATMUL_BLOCK_M);
+  const int64_t col_tiles = (out_features + 127) / 128;
+  const int64_t blocks = (cap + 7) / 8 * 8 * col_tiles;
+  if (cap > INT32_MAX || blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
+  const GridWorkspace w = grid_workspace(num_seqs, cap);
+  if (workspace_bytes < w.bytes) return VLP_ERR_CAPACITY;
+  if (cap == 0) return VLP_OK;
+
+  char* base = static_cast<char*>(workspace);
+  int32_t* bo = reinterpret_cast<int32_t*>(base + w.off_bo);
+  int32_t* gm = reinterpret_cast<int32_t*>(base + w.off_gm);
+  int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  vlp_status st = hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, VLP_MATMUL_BLOCK_M, bo, gm, to, cap, s));
+  if (st != VLP_OK) return st;
+  vlp::MatmulArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.bias = bias;
+  a.y = y;
+  a.cu = cu_seqlens;
+  a.grid_mapping = gm;
+  a.block_offsets = bo;
+  a.num_seqs = num_seqs;
+  a.k = in_features;
+  a.n = out_features;
+  a.grid_cap = static_cast<int32_t>(cap);
+  a.col_tiles = static_cast<int32_t>(col_tiles);
+  a.w_seq_stride = weight_seq_stride;
+  a.b_seq_stride = bias_seq_stride;
+  return hip_status(vlp::launch_ragged_matmul(dtype, a, bias != nullptr, blocks, s));
+}

@@ -73,6 +73,24 @@ struct BwdArgs {
   int32_t dkv_stride;          // dk and dv
 };
 
+// Arguments of one ragged matrix multiplication launch.
+struct MatmulArgs {
+  const void* x;               // [rows, k]
+  const void* w;               // [num_seqs or 1, n, k]
+  const void* bias;            // [num_seqs or 1, n] or nullptr
+  void* y;                     // [rows, n]
+  const int32_t* cu;           // [num_seqs + 1]
+  const int32_t* grid_mapping; // ragged grid over cu with VLP_MATMUL_BLOCK_M rows per tile
+  const int32_t* block_offsets;
+  int32_t num_seqs;
+  int32_t k;
+  int32_t n;
+  int32_t grid_cap;
+  int32_t col_tiles;           // ceil(n / 128)
+  int64_t w_seq_stride;        // elements between sequences' weights (0: shared)
+  int64_t b_seq_stride;        // elements between sequences' biases (0: shared)
+};
+
 // Kernel families and their tile shapes.  block_m is the query rows per
 // workgroup tile; it is what the ragged grid is built with.
 struct TileShape {
@@ -101,6 +119,9 @@ hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, i
 hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+
+// Ragged matrix multiplication, `blocks` workgroups.
+hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s);
 
 // Device ragged-grid build (one workgroup).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
