@@ -486,7 +486,7 @@ extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
   if (rows > INT32_MAX) return VLP_ERR_OVERFLOW;
   const int64_t cap = vlp_grid_capacity(rows, num_seqs, VLP_MATMUL_BLOCK_M);
-  const int64_t col_tiles = (out_features + 127) / 128;
+  const int64_t col_tiles = (out_features + vlp::kMatmulBlockN - 1) / vlp::kMatmulBlockN;
   const int64_t blocks = (cap + 7) / 8 * 8 * col_tiles;
   if (cap > INT32_MAX || blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
   const GridWorkspace w = grid_workspace(num_seqs, cap);

@@ -44,23 +44,27 @@ template <> __device__ __forceinline__ void widen_pair<VLP_FP16>(uint32_t x, flo
   hi = static_cast<float>(h[1]);
 }
 
-constexpr int kMmBM = VLP_MATMUL_BLOCK_M;  // token rows per tile (the ragged grid's block_m)
-constexpr int kMmBN = 128;  // output columns per tile
-constexpr int kMmBK = 64;   // in_features per LDS stage
+constexpr int kMmBK = 64;  // in_features per LDS stage
 
-template <int DT, bool BIAS>
-__global__ __launch_bounds__(256, 2) void ragged_matmul_h16(const MatmulArgs a) {
+// BM token rows x BN output columns per workgroup, WGM x WGN wavefronts each
+// owning (BM / WGM) tokens x (BN / WGN) columns.
+template <int DT, bool BIAS, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged_matmul_h16(const MatmulArgs a) {
   using E = Half16<DT>;
-  constexpr int RB = kMmBK * 2;        // bytes per tile row
-  constexpr int CPR = RB / 16;         // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;        // rows per 1 KB direct load
-  constexpr int LPT = kMmBM / RPI;     // loads per tile
-  constexpr int LPW = LPT / 4;         // per wave
-  constexpr int TILE = kMmBM * RB;     // bytes of one tile (W and x tiles have 128 rows each)
-  static_assert(kMmBM == kMmBN, "one load pattern serves both tiles");
+  constexpr int NW = WGM * WGN;
+  constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  constexpr int MI = TM / 32, NI = TN / 32;    // 32 x 32 MFMA tiles per wave
+  constexpr int RB = kMmBK * 2;                // bytes per tile row
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                // rows per 1 KB direct load
+  constexpr int LW = BN / RPI, LX = BM / RPI;  // loads per W / x tile
+  static_assert((LW + LX) % NW == 0, "tile loads must split evenly over the waves");
+  constexpr int LPW = (LW + LX) / NW;
+  constexpr int TW = BN * RB, TX = BM * RB;    // tile bytes
+  constexpr int STAGE = TW + TX;
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // W tile, x tile
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char lds0[STAGE];  // W tile, x tile
+  __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
 
   // Workgroup -> (row slot, column tile), XCD-aware (see the header).
   const int b = static_cast<int>(blockIdx.x);
@@ -73,26 +77,27 @@ __global__ __launch_bounds__(256, 2) void ragged_matmul_h16(const MatmulArgs a) 
   if (seq < 0 || seq >= a.num_seqs) return;
   const int tile = slot - a.block_offsets[seq];
   const int r_start = a.cu[seq];
-  const int row0 = tile * kMmBM;
-  const int nrows = min(kMmBM, a.cu[seq + 1] - r_start - row0);
-  const int n0 = nt * kMmBN;
-  const int ncols = min(kMmBN, a.n - n0);
+  const int row0 = tile * BM;
+  const int nrows = min(BM, a.cu[seq + 1] - r_start - row0);
+  const int n0 = nt * BN;
+  const int ncols = min(BN, a.n - n0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int wn = wave & 1;   // 64-column half of the tile
-  const int wm = wave >> 1;  // 64-token half of the tile
+  const int wn = wave % WGN;
+  const int wm = wave / WGN;
   const int k_bytes = a.k * 2;
 
-  // Direct-load offsets (the same for both tiles: rows are k_bytes apart).
+  // Direct loads: load j < LW fills W rows j*RPI.., the rest x rows; rows of
+  // both are k_bytes apart, so the lane offsets have one form.
   int voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int j = wave * LPW + i;
-    const int r = j * RPI + lane / CPR;
+    const int r = (j < LW ? j : j - LW) * RPI + lane / CPR;
     voff[i] = r * k_bytes + (((lane % CPR) ^ chunk_swz<64>(r)) << 4);
   }
   // Operand offsets within a 32-row sub-tile: row (lane & 31), chunk 2ks + hh.
@@ -115,34 +120,35 @@ __global__ __launch_bounds__(256, 2) void ragged_matmul_h16(const MatmulArgs a) 
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
       const int vo = voff[i];  // (a local copy: passing voff[i] directly drops the host-side kernel stub)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (VLP_LDS void*)(buf + TILE + j * 1024), 16, vo, 0, 0, 0);
+      if (j < LW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (VLP_LDS void*)(buf + j * 1024), 16, vo, 0, 0, 0);
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[NI][MI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < MI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   auto compute_stage = [&](const char* buf) {
-    const char* wt = buf + (64 * wn) * RB;
-    const char* xt = buf + TILE + (64 * wm) * RB;
+    const char* wt = buf + (TN * wn) * RB;
+    const char* xt = buf + TW + (TM * wm) * RB;
 #pragma unroll
     for (int ks = 0; ks < kMmBK / 16; ++ks) {
-      u32x4_t aop[2], bop[2];
+      u32x4_t aop[NI], bop[MI];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        aop[i] = *reinterpret_cast<const u32x4_t*>(wt + 32 * i * RB + ooff[ks]);
-        bop[i] = *reinterpret_cast<const u32x4_t*>(xt + 32 * i * RB + ooff[ks]);
-      }
+      for (int i = 0; i < NI; ++i) aop[i] = *reinterpret_cast<const u32x4_t*>(wt + 32 * i * RB + ooff[ks]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < MI; ++j) bop[j] = *reinterpret_cast<const u32x4_t*>(xt + 32 * j * RB + ooff[ks]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = E::mfma(aop[i], bop[j], acc[i][j]);
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < MI; ++j) acc[i][j] = E::mfma(aop[i], bop[j], acc[i][j]);
     }
   };
 
@@ -162,19 +168,20 @@ __global__ __launch_bounds__(256, 2) void ragged_matmul_h16(const MatmulArgs a) 
     __syncthreads();
   }
 
-  // Epilogue: lane holds token m = 64wm + 32j + n and, per register group q,
-  // output columns 64wn + 32i + 8q + 4hh + 0..3.
-  const char* bias_row = BIAS ? static_cast<const char*>(a.bias) + static_cast<size_t>(seq) * a.b_seq_stride * 2 : nullptr;
+  // Epilogue: lane holds token m = TM*wm + 32j + n and, per register group q,
+  // output columns TN*wn + 32i + 8q + 4hh + 0..3.
+  const char* bias_row =
+      BIAS ? static_cast<const char*>(a.bias) + static_cast<size_t>(seq) * a.b_seq_stride * 2 : nullptr;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = 64 * wm + 32 * j + n;
+  for (int j = 0; j < MI; ++j) {
+    const int m = TM * wm + 32 * j + n;
     if (m >= nrows) continue;
     uint16_t* yrow = static_cast<uint16_t*>(a.y) + (static_cast<size_t>(r_start) + row0 + m) * a.n + n0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = 64 * wn + 32 * i + 8 * q + 4 * hh;
+        const int col = TN * wn + 32 * i + 8 * q + 4 * hh;
         if (col >= ncols) continue;
         float v[4];
 #pragma unroll
@@ -197,14 +204,23 @@ __global__ __launch_bounds__(256, 2) void ragged_matmul_h16(const MatmulArgs a) 
   }
 }
 
+// Tile shape of the launch (the ragged grid's block_m is VLP_MATMUL_BLOCK_M).
+constexpr int kMmBM = VLP_MATMUL_BLOCK_M;
+constexpr int kMmBN = kMatmulBlockN;
+constexpr int kMmWGM = kMatmulWavesM;
+constexpr int kMmWGN = kMatmulWavesN;
+
 namespace {
 
 template <int DT>
 hipError_t go(const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s) {
+  constexpr int threads = kMmWGM * kMmWGN * 64;
   if (bias)
-    hipLaunchKernelGGL((ragged_matmul_h16<DT, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ragged_matmul_h16<DT, true, kMmBM, kMmBN, kMmWGM, kMmWGN>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(threads), 0, s, a);
   else
-    hipLaunchKernelGGL((ragged_matmul_h16<DT, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ragged_matmul_h16<DT, false, kMmBM, kMmBN, kMmWGM, kMmWGN>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -73,6 +73,13 @@ struct BwdArgs {
   int32_t dkv_stride;          // dk and dv
 };
 
+// Ragged matrix multiplication tiles: VLP_MATMUL_BLOCK_M token rows x
+// kMatmulBlockN output columns per workgroup, kMatmulWavesM x kMatmulWavesN
+// wavefronts.
+constexpr int kMatmulBlockN = 128;
+constexpr int kMatmulWavesM = 2;
+constexpr int kMatmulWavesN = 2;
+
 // Arguments of one ragged matrix multiplication launch.
 struct MatmulArgs {
   const void* x;               // [rows, k]
@@ -86,7 +93,7 @@ struct MatmulArgs {
   int32_t k;
   int32_t n;
   int32_t grid_cap;
-  int32_t col_tiles;           // ceil(n / 128)
+  int32_t col_tiles;           // ceil(n / kMatmulBlockN)
   int64_t w_seq_stride;        // elements between sequences' weights (0: shared)
   int64_t b_seq_stride;        // elements between sequences' biases (0: shared)
 };
