@@ -20,6 +20,12 @@ definition from the pages:
                              per sequence); "gigl.nn.packed_attention" (each
                              sequence attends only to itself; first-token
                              queries).
+* ``cu_seqlens_from_ids`` -- run boundaries of per-token document ids, with a
+                             fixed-capacity tail ("So you wanna CUDA Graph",
+                             "Terminology time").
+* ``document_masked_attention`` -- attention over one packed sequence under
+                             the sample-id mask, the dense definition that
+                             varlen attention must equal.
 * ``ragged_matmul``       -- "PyCoRa", "Ragged Matrix Multiplication" (each
                              sequence times its own weight matrix); a shared
                              weight gives the packed projections of
@@ -37,6 +43,8 @@ All pins are in ``tests/test_oracle.py``; no oracle function is "parity unpinned
 from .varlen_oracle import (  # noqa: F401
     INT32_MAX,
     build_ragged_grid,
+    cu_seqlens_from_ids,
+    document_masked_attention,
     decode_tile,
     grid_capacity,
     pack_sequences,

@@ -437,3 +437,50 @@ def ragged_matmul(x, weight, cu_seqlens, bias=None, shared_weight=False, shared_
         if b64 is not None:
             y[r0:r1] += b64 if shared_bias else b64[i]
     return y
+
+
+# ---------------------------------------------------------------------------
+# Document ids -> cu_seqlens ("DanLing NestedTensor" 3.3: varlen kernels
+# consume the partitions' segment boundaries; "So you wanna CUDA Graph",
+# "Terminology time": a fixed-capacity cu_seqlens ends in repeated totals
+# for the unused slots)
+# ---------------------------------------------------------------------------
+
+def cu_seqlens_from_ids(ids, max_seqs: int):
+    """Boundaries of the runs of equal ids in one packed sequence.
+
+    ``ids`` [T] integers: tokens of one document are contiguous, and a change
+    of id between neighbouring tokens starts a new sequence.  Returns
+    (cu [max_seqs + 1] int32 with cu[0] = 0, the run starts, then T repeated
+    for the unused slots; num_seqs).  Raises if there are more runs than
+    max_seqs.
+    """
+    ids = [int(x) for x in np.asarray(ids).reshape(-1).tolist()]
+    starts = [t for t in range(len(ids)) if t == 0 or ids[t] != ids[t - 1]]
+    if len(starts) > max_seqs:
+        raise ValueError("more runs than max_seqs")
+    cu = starts + [len(ids)] * (max_seqs + 1 - len(starts))
+    return np.asarray(cu, dtype=np.int32), len(starts)
+
+
+def document_masked_attention(q, k, v, ids, scale: float, causal: bool = False):
+    """Attention over one packed sequence of T tokens in which query p may
+    see key j only if ids[p] == ids[j] (and j <= p when causal): the
+    sample-id mask, written as a [T, T] mask over the whole sequence rather
+    than per sequence.  Returns (out [T, H, D], lse [H, T]) in float64."""
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    ids = np.asarray(ids).reshape(-1)
+    t, heads, _ = q64.shape
+    same = ids[:, None] == ids[None, :]
+    if causal:
+        same = same & np.tril(np.ones((t, t), dtype=bool))
+    out = np.zeros((t, heads, v64.shape[2]))
+    lse = np.full((heads, t), -np.inf)
+    for h in range(heads):
+        s = scale * (q64[:, h] @ k64[:, h].T)
+        m = np.where(same, s, -np.inf).max(axis=1)
+        w = np.where(same, np.exp(s - m[:, None]), 0.0)
+        den = w.sum(axis=1)
+        out[:, h] = (w @ v64[:, h]) / den[:, None]
+        lse[h] = m + np.log(den)
+    return out, lse
