@@ -439,6 +439,34 @@ vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, c
                              int32_t out_features, int64_t weight_seq_stride, int64_t bias_seq_stride, void* y,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * vlp_cu_seqlens_from_ids -- cu_seqlens of the runs of equal document ids in
+ * one packed sequence, built on the GPU (one workgroup, enqueued on `stream`,
+ * no host read).
+ *
+ * A query attending only to keys of its own document (the sample-id mask of
+ * one packed sequence) is varlen attention over the runs ("DanLing
+ * NestedTensor" 3.3: varlen kernels take the segment boundaries).  Tokens of
+ * a document must be contiguous: a change of id between neighbouring tokens
+ * starts a new sequence, so an id that comes back after another document
+ * starts a separate sequence.  The result has a fixed capacity ("So you
+ * wanna CUDA Graph", "Terminology time"): cu_seqlens[0..n-1] are the run
+ * starts, cu_seqlens[n..max_seqs] = num_tokens (zero-length sequences that
+ * every kernel here skips), so it can be passed on with num_seqs = max_seqs.
+ *
+ *   ids            device int32 [num_tokens] (may be NULL when num_tokens is 0).
+ *   max_seqs       >= 1, the capacity.
+ *   cu_seqlens     device int32 [max_seqs + 1].
+ *   num_seqs       device int32 [1]: receives the number of runs n.  If n >
+ *                  max_seqs only the first max_seqs starts are written and
+ *                  cu_seqlens must not be used.
+ * Errors: NULL cu_seqlens / num_seqs (or ids with num_tokens > 0) ->
+ * VLP_ERR_NULL; num_tokens < 0, max_seqs < 1 -> VLP_ERR_INVALID; num_tokens
+ * beyond int32 -> VLP_ERR_OVERFLOW; launch failure -> VLP_ERR_HIP.
+ */
+vlp_status vlp_cu_seqlens_from_ids(const int32_t* ids, int64_t num_tokens, int32_t max_seqs, int32_t* cu_seqlens,
+                                   int32_t* num_seqs, void* stream);
+
 /* vlp_status_string -- a static, human-readable name for a status code; for
  * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */
 const char* vlp_status_string(vlp_status status);

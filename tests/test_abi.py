@@ -370,6 +370,16 @@ def test_ragged_matmul_validation_errors():
     assert lib.vlp_ragged_matmul_workspace_size(0, 10, ctypes.addressof(nb)) == 2
 
 
+def test_cu_seqlens_from_ids_validation_errors():
+    lib = _lib.load()
+    assert lib.vlp_cu_seqlens_from_ids(None, 10, 4, FAKE, FAKE, None) == 1
+    assert lib.vlp_cu_seqlens_from_ids(FAKE, 10, 4, None, FAKE, None) == 1
+    assert lib.vlp_cu_seqlens_from_ids(FAKE, 10, 4, FAKE, None, None) == 1
+    assert lib.vlp_cu_seqlens_from_ids(FAKE, -1, 4, FAKE, FAKE, None) == 2
+    assert lib.vlp_cu_seqlens_from_ids(FAKE, 10, 0, FAKE, FAKE, None) == 2
+    assert lib.vlp_cu_seqlens_from_ids(FAKE, 2**31, 4, FAKE, FAKE, None) == 5
+
+
 def test_device_grid_validation_errors():
     lib = _lib.load()
     assert lib.vlp_build_ragged_grid_device(None, 2, 64, FAKE, FAKE, FAKE, 4, None) == 1

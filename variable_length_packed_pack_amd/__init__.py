@@ -16,6 +16,8 @@ Functions mirror the pages' calls:
 * ``varlen_attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k,
   max_seqlen, scale, causal) -> (dq, dk, dv)``, the gradients of the same
   attention ("gigl.nn.packed_attention", "Why this exists").
+* ``cu_seqlens_from_ids(ids, max_seqs) -> (cu_seqlens, num_seqs)``: the runs
+  of document ids in one packed sequence, on the device.
 * ``ragged_matmul(x, weight, cu_seqlens, bias) -> y``: every sequence times its
   own weight matrix, or one shared weight ("PyCoRa", "Ragged Matrix
   Multiplication").
@@ -383,3 +385,18 @@ def ragged_matmul(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tenso
                                _stream_handle(x.device))
     _lib.check(st, "ragged_matmul")
     return out
+
+
+def cu_seqlens_from_ids(ids: torch.Tensor, max_seqs: int):
+    """Device cu_seqlens [max_seqs + 1] of the runs of equal ids in ``ids``
+    (int32 [T] on the device) and a device int32 [1] holding the run count;
+    unused slots hold T (zero-length sequences).  Enqueued on the current
+    stream, no host read."""
+    if not ids.is_cuda or ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 device vector")
+    cu = torch.empty(int(max_seqs) + 1, dtype=torch.int32, device=ids.device)
+    n = torch.empty(1, dtype=torch.int32, device=ids.device)
+    st = _lib.load().vlp_cu_seqlens_from_ids(_ptr(ids) if ids.numel() else None, int(ids.numel()), int(max_seqs),
+                                             _ptr(cu), _ptr(n), _stream_handle(ids.device))
+    _lib.check(st, "cu_seqlens_from_ids")
+    return cu, n

@@ -73,6 +73,7 @@ SIGNATURES = {
     "vlp_ragged_matmul": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp,
                                            _vp, ctypes.c_size_t, _vp]),
+    "vlp_cu_seqlens_from_ids": (ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 

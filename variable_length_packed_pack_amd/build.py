@@ -45,6 +45,7 @@ SOURCES = [
     "attn_bwd_f16.hip",
     "attn_bwd_f32.hip",
     "ragged_matmul.hip",
+    "seq_ids.hip",
 ]
 
 

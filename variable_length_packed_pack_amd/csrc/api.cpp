@@ -517,3 +517,12 @@ extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void
   a.b_seq_stride = bias_seq_stride;
   return hip_status(vlp::launch_ragged_matmul(dtype, a, bias != nullptr, blocks, s));
 }
+
+extern "C" vlp_status vlp_cu_seqlens_from_ids(const int32_t* ids, int64_t num_tokens, int32_t max_seqs,
+                                              int32_t* cu_seqlens, int32_t* num_seqs, void* stream) {
+  if (!cu_seqlens || !num_seqs || (num_tokens > 0 && !ids)) return VLP_ERR_NULL;
+  if (num_tokens < 0 || max_seqs < 1) return VLP_ERR_INVALID;
+  if (num_tokens > INT32_MAX) return VLP_ERR_OVERFLOW;
+  return hip_status(vlp::launch_ids_to_cu(ids, static_cast<int32_t>(num_tokens), max_seqs, cu_seqlens, num_seqs,
+                                          static_cast<hipStream_t>(stream)));
+}

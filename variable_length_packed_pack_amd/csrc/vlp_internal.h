@@ -130,6 +130,10 @@ hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal,
 // Ragged matrix multiplication, `blocks` workgroups.
 hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s);
 
+// Document ids -> cu_seqlens with a fixed capacity (one workgroup).
+hipError_t launch_ids_to_cu(const int32_t* ids, int32_t num_tokens, int32_t max_seqs, int32_t* cu, int32_t* num_out,
+                            hipStream_t s);
+
 // Device ragged-grid build (one workgroup).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                              int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
