@@ -81,6 +81,17 @@ def algorithmic_flops(lengths: np.ndarray, heads: int, head_dim: int, causal: bo
     return f / 2 if causal else f
 
 
+def workload_flops(wl, heads: int, first_token: bool = False) -> float:
+    """Algorithmic forward flops of a workload: 4 * sum Lq_i * Lk_i * H * D
+    when query and key lengths differ (non-causal), else algorithmic_flops."""
+    if wl.lengths_q is not None and not first_token:
+        lq = wl.lengths_q.astype(np.float64)
+        lk = wl.lengths.astype(np.float64)
+        assert not wl.causal
+        return 4.0 * float(np.sum(lq * lk)) * heads * wl.head_dim
+    return algorithmic_flops(wl.lengths, heads, wl.head_dim, wl.causal, first_token=first_token)
+
+
 def compulsory_bytes(rows_q: int, total_k: int, heads: int, head_dim: int, elt: int) -> float:
     """q, k, v read once, out written once, lse written once."""
     return (2.0 * rows_q + 2.0 * total_k) * heads * head_dim * elt + 4.0 * rows_q * heads
@@ -106,6 +117,7 @@ def cpu_oracle_baseline(wl, budget_s: float, first_token: bool = False):
     import oracle  # test infrastructure: used only for this reported baseline
 
     cu = wl.cu_seqlens_host()
+    cu_q = wl.cu_seqlens_q_host()
     rows = cu[:-1].astype(np.int64)
     elapsed, heads_done = 0.0, 0
     while heads_done < wl.heads and (heads_done == 0 or elapsed < budget_s):
@@ -116,11 +128,11 @@ def cpu_oracle_baseline(wl, budget_s: float, first_token: bool = False):
         if first_token:
             q = q[rows]
         t0 = time.perf_counter()
-        oracle.varlen_attention(q, k, v, None if first_token else cu, cu, wl.scale, wl.causal,
+        oracle.varlen_attention(q, k, v, None if first_token else cu_q, cu, wl.scale, wl.causal,
                                 query_is_first_token=first_token)
         elapsed += time.perf_counter() - t0
         heads_done += 1
-    flops = algorithmic_flops(wl.lengths, heads_done, wl.head_dim, wl.causal, first_token=first_token)
+    flops = workload_flops(wl, heads_done, first_token=first_token)
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -149,6 +161,9 @@ def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
     b, h, d = wl.num_seqs, wl.heads, wl.head_dim
     lmax = wl.max_len
     cu = wl.cu_seqlens_host()
+    cross = wl.lengths_q is not None and not first_token
+    cu_q = wl.cu_seqlens_q_host()
+    lqmax = int(wl.query_lengths().max())
     elt = q.element_size()
     per_seq = 4 * h * lmax * d * elt
     chunk = max(1, min(b, int(40e9 // per_seq)))
@@ -159,10 +174,18 @@ def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
         nb = c1 - c0
         kp = torch.zeros(nb, h, lmax, d, dtype=q.dtype, device=q.device)
         vp = torch.zeros_like(kp)
-        qp = q[c0:c1].unsqueeze(2).contiguous() if first_token else torch.zeros_like(kp)
+        if first_token:
+            qp = q[c0:c1].unsqueeze(2).contiguous()
+        elif cross:
+            qp = torch.zeros(nb, h, lqmax, d, dtype=q.dtype, device=q.device)
+        else:
+            qp = torch.zeros_like(kp)
         for j, i in enumerate(range(c0, c1)):
             s, e = int(cu[i]), int(cu[i + 1])
-            if not first_token:
+            if cross:
+                qs, qe = int(cu_q[i]), int(cu_q[i + 1])
+                qp[j, :, : qe - qs] = q[qs:qe].transpose(0, 1)
+            elif not first_token:
                 qp[j, :, : e - s] = q[s:e].transpose(0, 1)
             kp[j, :, : e - s] = k[s:e].transpose(0, 1)
             vp[j, :, : e - s] = v[s:e].transpose(0, 1)
@@ -295,6 +318,10 @@ def padded_backward_comparator(wl, q, k, v, dout, reps: int):
 def bench_backward(args, wl, dev) -> int:
     """The gradient step; see the module docstring."""
     import torch
+
+    if wl.lengths_q is not None:
+        print("--backward runs on workloads whose query and key lengths agree", file=sys.stderr)
+        return 2
 
     import variable_length_packed_pack_amd as vlp
     import workloads
@@ -532,7 +559,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="zipf", help="tiny | graph | encoder | zipf | skewed")
+    ap.add_argument("--workload", default="zipf", help="tiny | graph | encoder | zipf | skewed | cross")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded SDPA comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
@@ -590,21 +617,29 @@ def main() -> int:
         # one query per sequence: the row cu_seqlens[i] of the packed batch
         q = q[torch.from_numpy(wl.cu_seqlens_host()[:-1]).long().to(dev)].contiguous()
     rows_q = q.shape[0]
-    flops = algorithmic_flops(wl.lengths, h, d, wl.causal, first_token=ft)
+    flops = workload_flops(wl, h, first_token=ft)
     out = torch.empty_like(q)
     lse = torch.empty(h, rows_q, dtype=torch.float32, device=dev)
     bm = vlp.kernel_block_m(q.dtype, d, wl.causal, ft, b, rows_q, wl.max_len)
     ws = torch.empty(vlp.workspace_size(b, rows_q, bm), dtype=torch.uint8, device=dev)
     cu_dev = torch.empty(b + 1, dtype=torch.int32, device=dev)
     lengths_host = wl.lengths.copy()
+    cross = wl.lengths_q is not None and not ft
+    cu_q_dev = torch.empty(b + 1, dtype=torch.int32, device=dev) if cross else cu_dev
+    lengths_q_host = wl.query_lengths().copy()
     n_steps = args.warmup + args.steps
     pinned = [torch.empty(b + 1, dtype=torch.int32).pin_memory() for _ in range(n_steps)]
+    pinned_q = [torch.empty(b + 1, dtype=torch.int32).pin_memory() for _ in range(n_steps)] if cross else None
 
     def step(i: int) -> None:
         flat, cu = vlp.pack_sequences(lengths_host, wl.max_len)
         pinned[i].copy_(cu)
         cu_dev.copy_(pinned[i], non_blocking=True)
-        vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
+        if cross:  # query boundaries of their own
+            _, cuq = vlp.pack_sequences(lengths_q_host, int(lengths_q_host.max()))
+            pinned_q[i].copy_(cuq)
+            cu_q_dev.copy_(pinned_q[i], non_blocking=True)
+        vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                             workspace=ws)
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -626,7 +661,7 @@ def main() -> int:
 
     # attention kernel alone: cached device grid, HIP events on the launch stream
     cu_host = torch.from_numpy(wl.cu_seqlens_host())
-    grid_host = vlp.build_ragged_grid(cu_host, bm)
+    grid_host = vlp.build_ragged_grid(cu_host if ft else torch.from_numpy(wl.cu_seqlens_q_host()), bm)
     grid = vlp.RaggedGrid(grid_host.grid_mapping.to(dev), grid_host.block_offsets.to(dev),
                           grid_host.tile_order.to(dev), grid_host.num_blocks, bm)
     stream = torch.cuda.Stream(device=dev)
@@ -634,12 +669,12 @@ def main() -> int:
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(3):
-            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
+            vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                                 grid=grid)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for _ in range(reps):
-            vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
+            vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
                                 grid=grid)
         ev1.record(stream)
     stream.synchronize()
@@ -695,9 +730,12 @@ def main() -> int:
                 "encoder": "128 sequences, gamma(2,75) lengths clipped to [8,384], 12 heads x 64, bf16",
                 "graph": "512 sequences, lognormal(ln 80, 0.6) lengths clipped to [1,256], 8 heads x 64, fp32",
                 "tiny": "8 sequences, U[1,64] lengths, 2 heads x 16, fp32",
+                "cross": "cross-attention: the zipf key lengths (65,536 keys over 64 sequences), ceil(len/4) "
+                         "queries each (16,408), 16 heads x 128, non-causal, bf16",
             }[wl.name],
             "num_seqs": b,
             "total_tokens": t,
+            "total_queries": rows_q,
             "max_seqlen": lmax,
             "heads": h,
             "head_dim": d,
@@ -716,7 +754,8 @@ def main() -> int:
         "algorithmic_gflop": round(flops / 1e9, 3),
         "compulsory_gb": round(nbytes / 1e9, 4),
         "rho_seq": round(t / (b * lmax), 4),
-        "work_ratio": round(float(np.sum(wl.lengths.astype(np.float64) ** 2)) / (b * lmax * lmax), 5),
+        "work_ratio": round(float(np.sum(wl.query_lengths().astype(np.float64) * wl.lengths))
+                            / (b * int(wl.query_lengths().max()) * lmax), 5),
         "pack_sequences_host_us": round(pack_us, 1),
         "cpu_baseline_detail": cpu,
     }

@@ -316,6 +316,27 @@ def test_strided_views_of_a_fused_projection(dtype, head_dim):
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
 
 
+def test_cross_attention_at_scale_sampled():
+    """The cross workload at full size (65,536 keys, 16,408 queries over 64
+    sequences, 16 x 128 bf16, non-causal) in the launch configuration the
+    benchmark times, checked on sampled rows."""
+    wl = workloads.make_workload(6)
+    cq, ck = wl.cu_seqlens_q_host(), wl.cu_seqlens_host()
+    out, lse = vlp.varlen_attn_fwd(wl.q.to(DEV), wl.k.to(DEV), wl.v.to(DEV), torch.from_numpy(cq).to(DEV),
+                                   torch.from_numpy(ck).to(DEV), wl.max_len, wl.scale, False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(88)
+    samples = [(int(rng.integers(0, wl.total_queries)), int(rng.integers(0, wl.heads))) for _ in range(64)]
+    samples += [(int(cq[i]), 3) for i in (0, 17, 63)] + [(int(cq[i + 1]) - 1, 9) for i in (0, 40)]
+    ref, ref_lse = oracle.varlen_attention_rows(wl.q, wl.k, wl.v, cq, ck, wl.scale, False, samples)
+    rows = torch.tensor([r for r, _ in samples], device=DEV)
+    heads = torch.tensor([h for _, h in samples], device=DEV)
+    err = np.max(np.abs(out[rows, heads].float().cpu().numpy() - ref))
+    lerr = np.max(np.abs(lse[heads, rows].cpu().numpy() - ref_lse))
+    _say(f"[parity] cross at scale, {len(samples)} sampled rows: out {err:.3e} lse {lerr:.3e}")
+    assert err <= TOL_OUT["bf16"] and lerr <= TOL_LSE
+
+
 def test_causal_with_longer_keys():
     """Lq != Lk (cross-attention shapes): bottom-right causal alignment."""
     rng = np.random.default_rng(14)

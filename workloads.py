@@ -28,6 +28,11 @@ use seed ``2000 + k`` for workload ``k``):
 5. skewed    -- 255 sequences uniform in [64, 256] followed by one sequence
                 of 32,768 tokens (placed last); bf16, 32 heads x 128, causal,
                 Q/K/V with standard deviation 0.5.
+6. cross     -- cross-attention at scale: the key lengths of workload 4 (the
+                Zipf split of 65,536 keys over 64 sequences) with ceil(len/4)
+                queries per sequence (16,408 queries); bf16, 16 heads x 128,
+                non-causal ("DanLing NestedTensor" 3.3: query and key lengths
+                may differ).
 
 Q, K and V are drawn together as float32 standard normals of shape
 ``[T, H, D]`` in the order q, k, v, scaled (workload 5 only), then rounded to
@@ -63,10 +68,11 @@ class Workload:
     heads: int
     head_dim: int
     causal: bool
-    lengths: np.ndarray      # int32 [B]
-    q: torch.Tensor | None   # [T, H, D] in ``dtype`` (CPU)
-    k: torch.Tensor | None
+    lengths: np.ndarray      # int32 [B] (key lengths; also the query lengths unless lengths_q is set)
+    q: torch.Tensor | None   # [T_q, H, D] in ``dtype`` (CPU)
+    k: torch.Tensor | None   # [T, H, D]
     v: torch.Tensor | None
+    lengths_q: np.ndarray | None = None  # int32 [B] query lengths when they differ
 
     @property
     def num_seqs(self) -> int:
@@ -95,6 +101,20 @@ class Workload:
         for n in self.lengths.tolist():
             out.append(out[-1] + int(n))
         return np.asarray(out, dtype=np.int32)
+
+    def query_lengths(self) -> np.ndarray:
+        return self.lengths if self.lengths_q is None else self.lengths_q
+
+    def cu_seqlens_q_host(self) -> np.ndarray:
+        """Query boundaries (the key boundaries unless the lengths differ)."""
+        out = [0]
+        for n in self.query_lengths().tolist():
+            out.append(out[-1] + int(n))
+        return np.asarray(out, dtype=np.int32)
+
+    @property
+    def total_queries(self) -> int:
+        return int(self.query_lengths().astype(np.int64).sum())
 
 
 def zipf_lengths(total_tokens: int, num_seqs: int, rng: np.random.Generator,
@@ -137,6 +157,8 @@ def draw_lengths(index: int) -> np.ndarray:
     elif index == 5:
         short = rng.integers(64, 257, size=255)
         lengths = np.concatenate([short, np.asarray([32768])])
+    elif index == 6:
+        return draw_lengths(4)
     else:
         raise ValueError(f"unknown workload {index}")
     return np.asarray(lengths, dtype=np.int32)
@@ -149,6 +171,7 @@ _SPECS = {
     3: ("encoder", "bf16", 12, 64, False, 1.0),
     4: ("zipf", "bf16", 16, 128, True, 1.0),
     5: ("skewed", "bf16", 32, 128, True, 0.5),
+    6: ("cross", "bf16", 16, 128, False, 1.0),
 }
 
 
@@ -181,9 +204,15 @@ def make_workload(index: int, with_values: bool = True,
         dtype = dtype_override
     lengths = draw_lengths(index)
     wl = Workload(name, index, dtype, heads, head_dim, causal, lengths, None, None, None)
+    if index == 6:
+        wl.lengths_q = ((lengths.astype(np.int64) + 3) // 4).astype(np.int32)
     if with_values:
-        wl.q, wl.k, wl.v = random_qkv(wl.total_tokens, heads, head_dim, dtype,
-                                      VALUE_SEED_BASE + index, std)
+        if wl.lengths_q is None:
+            wl.q, wl.k, wl.v = random_qkv(wl.total_tokens, heads, head_dim, dtype,
+                                          VALUE_SEED_BASE + index, std)
+        else:
+            wl.q, wl.k, wl.v = random_qkv(wl.total_queries, heads, head_dim, dtype,
+                                          VALUE_SEED_BASE + index, std, k_tokens=wl.total_tokens)
     return wl
 
 
