@@ -180,7 +180,8 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  * blocks": the output takes the query structure; query and key lengths may
  * differ).  Enqueues, on `stream`, the device grid build into `workspace`
  * (no host read of cu_seqlens) and one attention launch of
- * G_cap * heads workgroups in which surplus tiles exit at once.
+ * G_cap * heads workgroups in which surplus tiles exit at once (the static
+ * grid; vlp_varlen_attn_fwd_persistent launches fewer).
  *
  *   dtype          VLP_FP32, VLP_FP16 or VLP_BF16 for q, k, v and out; the
  *                  contractions accumulate in fp32, the softmax runs in fp32.
@@ -269,6 +270,33 @@ vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k,
                                     void* stream);
 
 /*
+ * vlp_varlen_attn_fwd_persistent -- vlp_varlen_attn_fwd with the persistent
+ * schedule of "So you wanna CUDA Graph" ("Graph overcapture: bound
+ * capacity-sized launches"): instead of one workgroup per capacity task
+ * (G_cap(rows_q, num_seqs, block_m) * heads, the surplus exiting at once),
+ * min(capacity tasks, W) workgroups are launched and each strides over the
+ * ACTIVE tasks (block_offsets[num_seqs] * heads, read on the device), so a
+ * launch recorded for a large token capacity costs what the real tokens
+ * need.  Every argument means what it means for vlp_varlen_attn_fwd, and
+ * the results are bit-identical to it (each task computes the same values).
+ *
+ *   num_workers    W; 0 = the number of workgroups of the kernel the device
+ *                  holds at once (compute units x workgroups per unit);
+ *                  > 0 = at most that many (a multiple of 8 keeps a
+ *                  sequence's tiles on one XCD's L2).
+ * Errors: as vlp_varlen_attn_fwd, plus num_workers < 0 -> VLP_ERR_INVALID.
+ */
+vlp_status vlp_varlen_attn_fwd_persistent(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                          int32_t heads, int32_t head_dim, int64_t q_row_stride,
+                                          int64_t kv_row_stride, int64_t out_row_stride,
+                                          int32_t max_seqlen, float scale, int32_t causal,
+                                          int32_t query_is_first_token, void* out, float* lse,
+                                          void* workspace, size_t workspace_bytes, int32_t num_workers,
+                                          void* stream);
+
+/*
  * Key rows per tile of the key grid that the dk/dv kernel of the backward
  * walks (for every dtype and head_dim).
  */
@@ -337,6 +365,26 @@ vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, cons
                                int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal,
                                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * vlp_varlen_attn_bwd_persistent -- vlp_varlen_attn_bwd with the persistent
+ * schedule (see vlp_varlen_attn_fwd_persistent): each of the two gradient
+ * launches has min(its capacity tasks, W) workgroups striding over its
+ * active tasks.  Arguments and results (bit-identical) as for
+ * vlp_varlen_attn_bwd; num_workers as for vlp_varlen_attn_fwd_persistent,
+ * W counted per launch.
+ * Errors: as vlp_varlen_attn_bwd, plus num_workers < 0 -> VLP_ERR_INVALID.
+ */
+vlp_status vlp_varlen_attn_bwd_persistent(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const void* out, const void* dout, const float* lse,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                          int64_t out_row_stride, int64_t dout_row_stride,
+                                          int64_t dq_row_stride, int64_t dkv_row_stride, int32_t max_seqlen,
+                                          float scale, int32_t causal, void* dq, void* dk, void* dv,
+                                          void* workspace, size_t workspace_bytes, int32_t num_workers,
+                                          void* stream);
 
 /*
  * vlp_varlen_attn_bwd_grid -- the same gradients with caller-supplied, cached
@@ -438,6 +486,20 @@ vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, c
                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows, int32_t in_features,
                              int32_t out_features, int64_t weight_seq_stride, int64_t bias_seq_stride, void* y,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vlp_ragged_matmul_persistent -- vlp_ragged_matmul with the persistent
+ * schedule (see vlp_varlen_attn_fwd_persistent): min(capacity tasks, W)
+ * workgroups stride over the (row tile, column tile) tasks of the active
+ * rows.  Arguments and results (bit-identical) as for vlp_ragged_matmul;
+ * num_workers as for vlp_varlen_attn_fwd_persistent.
+ * Errors: as vlp_ragged_matmul, plus num_workers < 0 -> VLP_ERR_INVALID.
+ */
+vlp_status vlp_ragged_matmul_persistent(int32_t dtype, const void* x, const void* weight, const void* bias,
+                                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows,
+                                        int32_t in_features, int32_t out_features, int64_t weight_seq_stride,
+                                        int64_t bias_seq_stride, void* y, void* workspace,
+                                        size_t workspace_bytes, int32_t num_workers, void* stream);
 
 /*
  * vlp_cu_seqlens_from_ids -- cu_seqlens of the runs of equal document ids in

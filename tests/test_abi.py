@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
     for must in ("vlp_pack_sequences", "vlp_build_ragged_grid", "vlp_varlen_attn_fwd",
                  "vlp_varlen_attn_fwd_grid", "vlp_build_ragged_grid_device", "vlp_grid_capacity",
                  "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string",
-                 "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size", "vlp_ragged_matmul"):
+                 "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size", "vlp_ragged_matmul",
+                 "vlp_varlen_attn_fwd_persistent", "vlp_varlen_attn_bwd_persistent", "vlp_ragged_matmul_persistent"):
         assert must in names
 
 
@@ -204,18 +205,43 @@ def test_kernel_block_m_and_workspace():
 FAKE = 0x10000  # aligned, never dereferenced: each case fails validation first
 
 
+# Which entry point the validation helpers call: None = the static grid,
+# an int = the persistent schedule with that num_workers.
+_WORKERS = [None]
+
+
+@pytest.fixture(params=[None, 0, 24], ids=["static", "persistent-resident", "persistent-24"], autouse=False)
+def schedule(request):
+    _WORKERS[0] = request.param
+    yield request.param
+    _WORKERS[0] = None
+
+
 def _fwd(**kw):
     lib = _lib.load()
     a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100, total_k=100, heads=2,
              head_dim=64, qs=0, kvs=0, os=0, max_seqlen=0, scale=0.125, causal=0, ft=0, out=FAKE, lse=None, ws=FAKE,
-             ws_bytes=1 << 20)
+             ws_bytes=1 << 20, workers=_WORKERS[0])
     a.update(kw)
-    return lib.vlp_varlen_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["b"], a["rows_q"],
-                                   a["total_k"], a["heads"], a["head_dim"], a["qs"], a["kvs"], a["os"],
-                                   a["max_seqlen"], a["scale"], a["causal"], a["ft"], a["out"], a["lse"], a["ws"],
-                                   a["ws_bytes"], None)
+    args = (a["dtype"], a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["b"], a["rows_q"], a["total_k"], a["heads"],
+            a["head_dim"], a["qs"], a["kvs"], a["os"], a["max_seqlen"], a["scale"], a["causal"], a["ft"], a["out"],
+            a["lse"], a["ws"], a["ws_bytes"])
+    if a["workers"] is None:
+        return lib.vlp_varlen_attn_fwd(*args, None)
+    return lib.vlp_varlen_attn_fwd_persistent(*args, a["workers"], None)
 
 
+def test_persistent_entry_points_reject_negative_worker_counts():
+    assert _fwd(workers=-1) == 2
+    assert _fwd(workers=-1, ws_bytes=16) == 2       # checked before anything else of the launch
+    assert _bwd(workers=-5) == 2
+    assert _mm(workers=-1) == 2
+    assert _fwd(workers=1, ws_bytes=16) == 4         # a positive count reaches the usual checks
+    assert _bwd(workers=7, ws_bytes=64) == 4
+    assert _mm(workers=3, ws_bytes=8) == 4
+
+
+@pytest.mark.usefixtures("schedule")
 def test_forward_validation_errors():
     assert _fwd(q=None) == 1
     assert _fwd(cu_k=None) == 1
@@ -269,14 +295,17 @@ def _bwd(**kw):
     lib = _lib.load()
     a = dict(dtype=2, q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, b=4, rows_q=100,
              total_k=100, heads=2, head_dim=64, strides=(0, 0, 0, 0, 0, 0), max_seqlen=0, scale=0.125, causal=0,
-             dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 20)
+             dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 20, workers=_WORKERS[0])
     a.update(kw)
-    return lib.vlp_varlen_attn_bwd(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["cu_q"],
-                                   a["cu_k"], a["b"], a["rows_q"], a["total_k"], a["heads"], a["head_dim"],
-                                   *a["strides"], a["max_seqlen"], a["scale"], a["causal"], a["dq"], a["dk"],
-                                   a["dv"], a["ws"], a["ws_bytes"], None)
+    args = (a["dtype"], a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["cu_q"], a["cu_k"], a["b"],
+            a["rows_q"], a["total_k"], a["heads"], a["head_dim"], *a["strides"], a["max_seqlen"], a["scale"],
+            a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"])
+    if a["workers"] is None:
+        return lib.vlp_varlen_attn_bwd(*args, None)
+    return lib.vlp_varlen_attn_bwd_persistent(*args, a["workers"], None)
 
 
+@pytest.mark.usefixtures("schedule")
 def test_backward_validation_errors():
     for name in ("q", "k", "v", "out", "dout", "lse", "cu_q", "cu_k", "dq", "dk", "dv", "ws"):
         assert _bwd(**{name: None}) == 1, name
@@ -345,12 +374,16 @@ def test_backward_workspace_size():
 def _mm(**kw):
     lib = _lib.load()
     a = dict(dtype=2, x=FAKE, w=FAKE, bias=None, cu=FAKE, b=4, rows=100, k=512, n=256, ws_=0, bs=0, y=FAKE, ws=FAKE,
-             ws_bytes=1 << 20)
+             ws_bytes=1 << 20, workers=_WORKERS[0])
     a.update(kw)
-    return lib.vlp_ragged_matmul(a["dtype"], a["x"], a["w"], a["bias"], a["cu"], a["b"], a["rows"], a["k"], a["n"],
-                                 a["ws_"], a["bs"], a["y"], a["ws"], a["ws_bytes"], None)
+    args = (a["dtype"], a["x"], a["w"], a["bias"], a["cu"], a["b"], a["rows"], a["k"], a["n"], a["ws_"], a["bs"],
+            a["y"], a["ws"], a["ws_bytes"])
+    if a["workers"] is None:
+        return lib.vlp_ragged_matmul(*args, None)
+    return lib.vlp_ragged_matmul_persistent(*args, a["workers"], None)
 
 
+@pytest.mark.usefixtures("schedule")
 def test_ragged_matmul_validation_errors():
     for name in ("x", "w", "cu", "y", "ws"):
         assert _mm(**{name: None}) == 1, name

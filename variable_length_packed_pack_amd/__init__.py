@@ -179,13 +179,17 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     max_seqlen: int = 0, scale: Optional[float] = None, causal: bool = False,
                     query_is_first_token: bool = False, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, *, return_lse: bool = True,
-                    workspace: Optional[torch.Tensor] = None, grid: Optional[RaggedGrid] = None):
+                    workspace: Optional[torch.Tensor] = None, grid: Optional[RaggedGrid] = None,
+                    num_workers: Optional[int] = None):
     """Packed attention forward on the current stream; returns (out, lse).
 
     q [rows_q, H, D] (first-token mode: [num_seqs, H, D]), k/v [T_k, H, D],
     cu_seqlens int32 [B+1] on the same device.  ``grid``: cached device
     metadata from ``build_ragged_grid`` (host-built arrays moved to the
-    device) to skip the device grid build.
+    device) to skip the device grid build.  ``num_workers``: None launches
+    the static grid (one workgroup per capacity tile and head); an int
+    launches the persistent schedule with that many workgroups at most (0 =
+    as many as the device holds at once), striding over the active tiles.
     """
     lib = _lib.load()
     if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens_k.is_cuda):
@@ -214,6 +218,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ft = int(bool(query_is_first_token))
     cu_q_ptr = None if (ft and cu_seqlens_q is None) else _ptr(cu_seqlens_q)
     stream = _stream_handle(dev)
+    if grid is not None and num_workers is not None:
+        raise ValueError("the persistent schedule builds its grid on the device: pass grid or num_workers")
     if grid is not None:
         nb = grid.num_blocks if grid.num_blocks is not None else int(grid.grid_mapping.numel())
         st = lib.vlp_varlen_attn_fwd_grid(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b,
@@ -230,11 +236,13 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_fwd")
         nbytes = workspace_size(b, b if ft else rows_q, bm)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    st = lib.vlp_varlen_attn_fwd(code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b, rows_q,
-                                 total_k, heads, head_dim, q_st, k_st, o_st, int(max_seqlen), float(scale),
-                                 int(bool(causal)), ft,
-                                 _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel()), stream)
-    _lib.check(st, "varlen_attn_fwd")
+    args = (code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim,
+            q_st, k_st, o_st, int(max_seqlen), float(scale), int(bool(causal)), ft, _ptr(out), _ptr(lse),
+            _ptr(workspace), int(workspace.numel()))
+    if num_workers is None:
+        _lib.check(lib.vlp_varlen_attn_fwd(*args, stream), "varlen_attn_fwd")
+    else:
+        _lib.check(lib.vlp_varlen_attn_fwd_persistent(*args, int(num_workers), stream), "varlen_attn_fwd_persistent")
     return out, lse
 
 
@@ -256,7 +264,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                     dv: Optional[torch.Tensor] = None, *, workspace: Optional[torch.Tensor] = None,
                     grids: Optional[tuple] = None, row_stats: Optional[torch.Tensor] = None,
-                    phases: int = 3):
+                    phases: int = 3, num_workers: Optional[int] = None):
     """Gradients (dq, dk, dv) of ``varlen_attn_fwd`` on the current stream.
 
     ``out`` and ``lse`` are the forward's results for the same arguments;
@@ -266,7 +274,8 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     ``build_ragged_grid`` over cu_seqlens_q with the kernel's block_m and over
     cu_seqlens_k with VLP_BWD_BLOCK_K; then ``row_stats`` (fp32 [2, H, rows_q]) carries the row
     statistics from the dq phase to the dk/dv phase and ``phases`` selects
-    VLP_BWD_DQ, VLP_BWD_DKDV or both.
+    VLP_BWD_DQ, VLP_BWD_DKDV or both.  ``num_workers``: as for
+    ``varlen_attn_fwd`` (device-built grids only), per gradient launch.
     """
     lib = _lib.load()
     tensors = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k)
@@ -300,6 +309,8 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         raise ValueError("dk and dv must share one token stride")
     strides = (q_st, k_st, o_st, do_st, dq_st, dk_st)
     code = _DTYPE_CODES[q.dtype]
+    if grids is not None and num_workers is not None:
+        raise ValueError("the persistent schedule builds its grids on the device: pass grids or num_workers")
     if grids is not None:
         gq, gk = grids
         if row_stats is None:
@@ -323,12 +334,14 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
             raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_bwd")
         nbytes = bwd_workspace_size(b, rows_q, total_k, heads, bm)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    st = lib.vlp_varlen_attn_bwd(code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
-                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim,
-                                 *strides, int(max_seqlen), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
-                                 _ptr(dv),
-                                 _ptr(workspace), int(workspace.numel()), _stream_handle(q.device))
-    _lib.check(st, "varlen_attn_bwd")
+    args = (code, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens_q),
+            _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim, *strides, int(max_seqlen), float(scale),
+            int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace.numel()))
+    stream = _stream_handle(q.device)
+    if num_workers is None:
+        _lib.check(lib.vlp_varlen_attn_bwd(*args, stream), "varlen_attn_bwd")
+    else:
+        _lib.check(lib.vlp_varlen_attn_bwd_persistent(*args, int(num_workers), stream), "varlen_attn_bwd_persistent")
     return dq, dk, dv
 
 
@@ -338,13 +351,14 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
 
 def ragged_matmul(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor,
                   bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, *,
-                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  workspace: Optional[torch.Tensor] = None, num_workers: Optional[int] = None) -> torch.Tensor:
     """y = x_i @ weight_i^T (+ bias_i) for the rows of every sequence i.
 
     x [rows, K] contiguous; weight [B, N, K] (one linear-layer weight per
     sequence) or [N, K] (shared); bias None, [B, N] or [N]; cu_seqlens int32
     [B+1] on the device.  Returns y [rows, N]; rows owned by no sequence are
     left as they were (fresh outputs come from ``torch.empty``).
+    ``num_workers``: as for ``varlen_attn_fwd``.
     """
     lib = _lib.load()
     if not (x.is_cuda and weight.is_cuda and cu_seqlens.is_cuda):
@@ -380,10 +394,13 @@ def ragged_matmul(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tenso
         nb = ctypes.c_size_t(0)
         _lib.check(lib.vlp_ragged_matmul_workspace_size(b, rows, ctypes.addressof(nb)), "ragged_matmul")
         workspace = torch.empty(max(int(nb.value), 256), dtype=torch.uint8, device=x.device)
-    st = lib.vlp_ragged_matmul(_DTYPE_CODES[x.dtype], _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), b, rows,
-                               k, n, w_stride, b_stride, _ptr(out), _ptr(workspace), int(workspace.numel()),
-                               _stream_handle(x.device))
-    _lib.check(st, "ragged_matmul")
+    args = (_DTYPE_CODES[x.dtype], _ptr(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), b, rows, k, n, w_stride,
+            b_stride, _ptr(out), _ptr(workspace), int(workspace.numel()))
+    if num_workers is None:
+        _lib.check(lib.vlp_ragged_matmul(*args, _stream_handle(x.device)), "ragged_matmul")
+    else:
+        _lib.check(lib.vlp_ragged_matmul_persistent(*args, int(num_workers), _stream_handle(x.device)),
+                   "ragged_matmul_persistent")
     return out
 
 

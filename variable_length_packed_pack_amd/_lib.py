@@ -51,6 +51,12 @@ SIGNATURES = {
                                              *[ctypes.c_int64] * 3,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                              _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "vlp_varlen_attn_fwd_persistent": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                        ctypes.c_int32, *[ctypes.c_int64] * 3,
+                                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                                        ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t,
+                                                        ctypes.c_int32, _vp]),
     "vlp_varlen_attn_fwd_grid": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                   *[ctypes.c_int64] * 3,
@@ -63,6 +69,12 @@ SIGNATURES = {
                                              ctypes.c_int32, *[ctypes.c_int64] * 6,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "vlp_varlen_attn_bwd_persistent": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                                        ctypes.c_int32, ctypes.c_int32, *[ctypes.c_int64] * 6,
+                                                        ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                                        _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_int32,
+                                                        _vp]),
     "vlp_varlen_attn_bwd_grid": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                                   ctypes.c_int32, *[ctypes.c_int64] * 6,
@@ -73,6 +85,10 @@ SIGNATURES = {
     "vlp_ragged_matmul": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp,
                                            _vp, ctypes.c_size_t, _vp]),
+    "vlp_ragged_matmul_persistent": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_size_t,
+                                                      ctypes.c_int32, _vp]),
     "vlp_cu_seqlens_from_ids": (ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }

@@ -120,16 +120,26 @@ vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32
 }
 
 vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int32_t causal, int32_t first_token,
-                   int64_t slots, hipStream_t s) {
+                   int64_t slots, int32_t workers, hipStream_t s) {
   if (slots <= 0) return VLP_OK;
-  if (first_token) return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0, slots, s));
+  if (first_token)
+    return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0, slots, workers, s));
   const int64_t blocks = slots * a.heads;
   if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
   switch (dtype) {
-    case VLP_BF16: return hip_status(vlp::launch_attn_bf16(a, head_dim, causal != 0, blocks, s));
-    case VLP_FP16: return hip_status(vlp::launch_attn_f16(a, head_dim, causal != 0, blocks, s));
-    default: return hip_status(vlp::launch_attn_f32(a, head_dim, causal != 0, blocks, s));
+    case VLP_BF16: return hip_status(vlp::launch_attn_bf16(a, head_dim, causal != 0, blocks, workers, s));
+    case VLP_FP16: return hip_status(vlp::launch_attn_f16(a, head_dim, causal != 0, blocks, workers, s));
+    default: return hip_status(vlp::launch_attn_f32(a, head_dim, causal != 0, blocks, workers, s));
   }
+}
+
+// The launch-width argument of the persistent entry points: 0 asks for the
+// resident workgroup count, a positive value caps the width; negative values
+// are out of contract.
+vlp_status persistent_workers(int32_t num_workers, int32_t* workers) {
+  if (num_workers < 0) return VLP_ERR_INVALID;
+  *workers = num_workers == 0 ? vlp::kResident : num_workers;
+  return VLP_OK;
 }
 
 // Workspace of the backward: [lse2 | delta | query grid | key grid], each
@@ -156,19 +166,19 @@ BwdWorkspace bwd_workspace(int32_t num_seqs, int64_t rows_q, int64_t total_k, in
 }
 
 vlp_status launch_bwd(int32_t dtype, bool dkdv, const vlp::BwdArgs& a, int32_t head_dim, bool causal,
-                      int64_t blocks, hipStream_t s) {
+                      int64_t blocks, int32_t workers, hipStream_t s) {
   if (blocks <= 0) return VLP_OK;
   if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
   switch (dtype) {
     case VLP_BF16:
-      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_bf16(a, head_dim, causal, blocks, s)
-                             : vlp::launch_attn_bwd_dq_bf16(a, head_dim, causal, blocks, s));
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_bf16(a, head_dim, causal, blocks, workers, s)
+                             : vlp::launch_attn_bwd_dq_bf16(a, head_dim, causal, blocks, workers, s));
     case VLP_FP16:
-      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f16(a, head_dim, causal, blocks, s)
-                             : vlp::launch_attn_bwd_dq_f16(a, head_dim, causal, blocks, s));
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f16(a, head_dim, causal, blocks, workers, s)
+                             : vlp::launch_attn_bwd_dq_f16(a, head_dim, causal, blocks, workers, s));
     default:
-      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f32(a, head_dim, causal, blocks, s)
-                             : vlp::launch_attn_bwd_dq_f32(a, head_dim, causal, blocks, s));
+      return hip_status(dkdv ? vlp::launch_attn_bwd_dkdv_f32(a, head_dim, causal, blocks, workers, s)
+                             : vlp::launch_attn_bwd_dq_f32(a, head_dim, causal, blocks, workers, s));
   }
 }
 
@@ -204,13 +214,14 @@ extern "C" vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, in
                                            grid_cap, static_cast<hipStream_t>(stream)));
 }
 
-extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
-                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
-                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
-                                          int64_t out_row_stride, int32_t max_seqlen, float scale, int32_t causal,
-                                          int32_t query_is_first_token, void* out, float* lse, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+namespace {
+
+vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                           int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                           int64_t out_row_stride, int32_t max_seqlen, float scale, int32_t causal,
+                           int32_t query_is_first_token, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, int32_t workers, void* stream) {
   Checked c{};
   vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
                                 head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
@@ -238,7 +249,35 @@ extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const vo
   a.block_offsets = bo;
   a.tile_order = to;
   a.grid_cap = static_cast<int32_t>(cap);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, s);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, s);
+}
+
+}  // namespace
+
+extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                          int64_t out_row_stride, int32_t max_seqlen, float scale, int32_t causal,
+                                          int32_t query_is_first_token, void* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return fwd_device_grid(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads, head_dim,
+                         q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
+                         query_is_first_token, out, lse, workspace, workspace_bytes, vlp::kStaticGrid, stream);
+}
+
+extern "C" vlp_status vlp_varlen_attn_fwd_persistent(
+    int32_t dtype, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads, int32_t head_dim,
+    int64_t q_row_stride, int64_t kv_row_stride, int64_t out_row_stride, int32_t max_seqlen, float scale,
+    int32_t causal, int32_t query_is_first_token, void* out, float* lse, void* workspace, size_t workspace_bytes,
+    int32_t num_workers, void* stream) {
+  int32_t workers = 0;
+  const vlp_status st = persistent_workers(num_workers, &workers);
+  if (st != VLP_OK) return st;
+  return fwd_device_grid(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads, head_dim,
+                         q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
+                         query_is_first_token, out, lse, workspace, workspace_bytes, workers, stream);
 }
 
 extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k, const void* v,
@@ -264,7 +303,7 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
   a.tile_order = tile_order;
   a.num_blocks = static_cast<int32_t>(num_blocks);
   a.grid_cap = static_cast<int32_t>(num_blocks);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks,
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -354,15 +393,16 @@ vlp::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const vo
 
 }  // namespace
 
-extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
-                                          const void* out, const void* dout, const float* lse,
-                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
-                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
-                                          int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
-                                          int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal,
-                                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+namespace {
+
+vlp_status bwd_device_grid(int32_t dtype, const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                           int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                           int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
+                           int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal, void* dq,
+                           void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t workers,
+                           void* stream) {
   Checked c{};
   int32_t do_stride = 0, dq_stride = 0, dkv_stride = 0;
   const BwdStrides sd{q_row_stride, kv_row_stride, out_row_stride, dout_row_stride, dq_row_stride, dkv_row_stride};
@@ -396,7 +436,7 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
     a.block_offsets = bo;
     a.tile_order = to;
     a.grid_cap = static_cast<int32_t>(w.cap_q);
-    st = launch_bwd(dtype, false, a, head_dim, causal != 0, w.cap_q * heads, s);
+    st = launch_bwd(dtype, false, a, head_dim, causal != 0, w.cap_q * heads, workers, s);
     if (st != VLP_OK) return st;
   }
   if (w.cap_k > 0) {
@@ -410,9 +450,42 @@ extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const vo
     a.block_offsets = bo;
     a.tile_order = to;
     a.grid_cap = static_cast<int32_t>(w.cap_k);
-    st = launch_bwd(dtype, true, a, head_dim, causal != 0, w.cap_k * heads, s);
+    st = launch_bwd(dtype, true, a, head_dim, causal != 0, w.cap_k * heads, workers, s);
   }
   return st;
+}
+
+}  // namespace
+
+extern "C" vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                          const void* out, const void* dout, const float* lse,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                          int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                          int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                          int64_t out_row_stride, int64_t dout_row_stride, int64_t dq_row_stride,
+                                          int64_t dkv_row_stride, int32_t max_seqlen, float scale, int32_t causal,
+                                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  return bwd_device_grid(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k,
+                         heads, head_dim, q_row_stride, kv_row_stride, out_row_stride, dout_row_stride,
+                         dq_row_stride, dkv_row_stride, max_seqlen, scale, causal, dq, dk, dv, workspace,
+                         workspace_bytes, vlp::kStaticGrid, stream);
+}
+
+extern "C" vlp_status vlp_varlen_attn_bwd_persistent(
+    int32_t dtype, const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+    int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride, int64_t out_row_stride,
+    int64_t dout_row_stride, int64_t dq_row_stride, int64_t dkv_row_stride, int32_t max_seqlen, float scale,
+    int32_t causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int32_t num_workers,
+    void* stream) {
+  int32_t workers = 0;
+  const vlp_status st = persistent_workers(num_workers, &workers);
+  if (st != VLP_OK) return st;
+  return bwd_device_grid(dtype, q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k,
+                         heads, head_dim, q_row_stride, kv_row_stride, out_row_stride, dout_row_stride,
+                         dq_row_stride, dkv_row_stride, max_seqlen, scale, causal, dq, dk, dv, workspace,
+                         workspace_bytes, workers, stream);
 }
 
 extern "C" vlp_status vlp_varlen_attn_bwd_grid(
@@ -449,7 +522,7 @@ extern "C" vlp_status vlp_varlen_attn_bwd_grid(
     a.block_offsets = q_block_offsets;
     a.tile_order = q_tile_order;
     a.grid_cap = static_cast<int32_t>(q_num_blocks);
-    st = launch_bwd(dtype, false, a, head_dim, causal != 0, q_num_blocks * heads, s);
+    st = launch_bwd(dtype, false, a, head_dim, causal != 0, q_num_blocks * heads, vlp::kStaticGrid, s);
     if (st != VLP_OK) return st;
   }
   if (run_dkdv) {
@@ -457,7 +530,7 @@ extern "C" vlp_status vlp_varlen_attn_bwd_grid(
     a.block_offsets = k_block_offsets;
     a.tile_order = k_tile_order;
     a.grid_cap = static_cast<int32_t>(k_num_blocks);
-    st = launch_bwd(dtype, true, a, head_dim, causal != 0, k_num_blocks * heads, s);
+    st = launch_bwd(dtype, true, a, head_dim, causal != 0, k_num_blocks * heads, vlp::kStaticGrid, s);
   }
   return st;
 }
@@ -469,11 +542,12 @@ extern "C" vlp_status vlp_ragged_matmul_workspace_size(int32_t num_seqs, int64_t
   return VLP_OK;
 }
 
-extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, const void* bias,
-                                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows,
-                                        int32_t in_features, int32_t out_features, int64_t weight_seq_stride,
-                                        int64_t bias_seq_stride, void* y, void* workspace, size_t workspace_bytes,
-                                        void* stream) {
+namespace {
+
+vlp_status matmul_device_grid(int32_t dtype, const void* x, const void* weight, const void* bias,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows, int32_t in_features,
+                              int32_t out_features, int64_t weight_seq_stride, int64_t bias_seq_stride, void* y,
+                              void* workspace, size_t workspace_bytes, int32_t workers, void* stream) {
   if (!x || !weight || !cu_seqlens || !y || !workspace) return VLP_ERR_NULL;
   if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
   if (dtype == VLP_FP32) return VLP_ERR_UNSUPPORTED;
@@ -515,7 +589,32 @@ extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void
   a.col_tiles = static_cast<int32_t>(col_tiles);
   a.w_seq_stride = weight_seq_stride;
   a.b_seq_stride = bias_seq_stride;
-  return hip_status(vlp::launch_ragged_matmul(dtype, a, bias != nullptr, blocks, s));
+  return hip_status(vlp::launch_ragged_matmul(dtype, a, bias != nullptr, blocks, workers, s));
+}
+
+}  // namespace
+
+extern "C" vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, const void* bias,
+                                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t rows,
+                                        int32_t in_features, int32_t out_features, int64_t weight_seq_stride,
+                                        int64_t bias_seq_stride, void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return matmul_device_grid(dtype, x, weight, bias, cu_seqlens, num_seqs, rows, in_features, out_features,
+                            weight_seq_stride, bias_seq_stride, y, workspace, workspace_bytes, vlp::kStaticGrid,
+                            stream);
+}
+
+extern "C" vlp_status vlp_ragged_matmul_persistent(int32_t dtype, const void* x, const void* weight,
+                                                   const void* bias, const int32_t* cu_seqlens, int32_t num_seqs,
+                                                   int64_t rows, int32_t in_features, int32_t out_features,
+                                                   int64_t weight_seq_stride, int64_t bias_seq_stride, void* y,
+                                                   void* workspace, size_t workspace_bytes, int32_t num_workers,
+                                                   void* stream) {
+  int32_t workers = 0;
+  const vlp_status st = persistent_workers(num_workers, &workers);
+  if (st != VLP_OK) return st;
+  return matmul_device_grid(dtype, x, weight, bias, cu_seqlens, num_seqs, rows, in_features, out_features,
+                            weight_seq_stride, bias_seq_stride, y, workspace, workspace_bytes, workers, stream);
 }
 
 extern "C" vlp_status vlp_cu_seqlens_from_ids(const int32_t* ids, int64_t num_tokens, int32_t max_seqs,

@@ -100,7 +100,7 @@ __device__ __forceinline__ void load_offsets_f32(int wave, int lane, int rs_byte
 // dQ (and delta, lse in exp2 units) over the query tiles, fp32.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
+__device__ __forceinline__ void attn_bwd_dq_f32_task(const BwdArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D % 16 == 0, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   constexpr int BM = 32 * NW;
@@ -115,13 +115,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   constexpr int LPW = LPT / NW;
   constexpr int TILE = BN * RB;
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
-
   BwdTile tc;
-  if (!decode_bwd<false>(a, tc)) return;
+  if (!decode_bwd<false>(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -241,11 +238,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   store_row_t_f32<D, DT32>(static_cast<float*>(a.dq) + qrow_g * a.dq_stride + hoff, acc, a.scale, hh);
 }
 
+template <int D, int NW, int BN, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * (BN * D * 4)];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * (BN * D * 4)];  // buffer 1
+  const int tasks = bwd_active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_bwd_dq_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_bwd_dq_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV over the key tiles, fp32.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(const BwdArgs a) {
+__device__ __forceinline__ void attn_bwd_dkdv_f32_task(const BwdArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D % 16 == 0, "head_dim");
   static_assert(BQ % 32 == 0 && BQ <= kStatRows, "query block");
   constexpr int BK = 32 * NW;
@@ -261,13 +276,10 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   constexpr int TILE = BQ * RB;
   constexpr int STATS = 2 * TILE;  // lse2[kStatRows], then delta[kStatRows]
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE + 8 * kStatRows];  // Q tile, dO tile, statistics
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE + 8 * kStatRows];
-
   BwdTile tc;
-  if (!decode_bwd<true>(a, tc)) return;
+  if (!decode_bwd<true>(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -406,6 +418,25 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   const size_t dkidx = krow_g * a.dkv_stride + hoff;
   store_row_t_f32<D, DT32>(static_cast<float*>(a.dk) + dkidx, dk, a.scale, hh);
   store_row_t_f32<D, DT32>(static_cast<float*>(a.dv) + dkidx, dv, 1.0f, hh);
+}
+
+template <int D, int NW, int BQ, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(const BwdArgs a) {
+  // Per buffer: Q tile, dO tile, statistics.
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * (BQ * D * 4) + 8 * kStatRows];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * (BQ * D * 4) + 8 * kStatRows];
+  const int tasks = bwd_active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_bwd_dkdv_f32_task<D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_bwd_dkdv_f32_task<D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
 }
 
 }  // namespace vlp

@@ -51,20 +51,26 @@ namespace vlp {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Workgroup -> (sequence, local tile) for a backward launch.  KEY_GRID: the
+// Task -> (sequence, local tile, head) for a backward launch.  KEY_GRID: the
 // grid was built over the key lengths, and local tiles run in mirrored order.
+// Tasks are laid out as in the forward (head fastest) and run as there: one
+// per workgroup on the static grid, blockIdx.x + j * gridDim.x on the
+// persistent grid.
 struct BwdTile {
   int seq, tile, head;
   int q_start, lq, k_start, lk;
 };
 
+__device__ __forceinline__ int bwd_active_tasks(const BwdArgs& a) {
+  const int g = min(a.block_offsets[a.num_seqs], a.grid_cap);
+  return g > 0 ? g * a.heads : 0;
+}
+
 template <bool KEY_GRID>
-__device__ __forceinline__ bool decode_bwd(const BwdArgs& a, BwdTile& t) {
+__device__ __forceinline__ bool decode_bwd(const BwdArgs& a, int task, BwdTile& t) {
   const int heads = a.heads;
-  const int slot = static_cast<int>(blockIdx.x) / heads;
-  t.head = static_cast<int>(blockIdx.x) - slot * heads;
-  const int g = a.block_offsets[a.num_seqs];
-  if (slot >= g || slot >= a.grid_cap) return false;
+  const int slot = task / heads;
+  t.head = task - slot * heads;
   const int f = a.tile_order ? a.tile_order[slot] : slot;
   if (f < 0 || f >= a.grid_cap) return false;  // out-of-contract metadata: skip, never read past it
   t.seq = a.grid_mapping[f];
@@ -214,7 +220,7 @@ __device__ __forceinline__ void store_row_t(uint16_t* rowp, const f32x16_t (&acc
 // dQ (and delta, lse in exp2 units) over the query tiles.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
+__device__ __forceinline__ void attn_bwd_dq_h16_task(const BwdArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   constexpr int BM = 32 * NW;
@@ -229,13 +235,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   constexpr int LPW = LPT / NW;
   constexpr int TILE = BN * RB;
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
-
   BwdTile tc;
-  if (!decode_bwd<false>(a, tc)) return;
+  if (!decode_bwd<false>(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -360,11 +363,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dq) + qrow_g * a.dq_stride + hoff, acc, a.scale, hh);
 }
 
+template <int DT, int D, int NW, int BN, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * (BN * D * 2)];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * (BN * D * 2)];  // buffer 1
+  const int tasks = bwd_active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_bwd_dq_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_bwd_dq_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV over the key tiles.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(const BwdArgs a) {
+__device__ __forceinline__ void attn_bwd_dkdv_h16_task(const BwdArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head_dim");
   static_assert(BQ % 64 == 0, "4-byte direct loads move the row statistics 64 rows at a time");
   constexpr int BK = 32 * NW;
@@ -380,13 +401,10 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   constexpr int TILE = BQ * RB;
   constexpr int STATS = 2 * TILE;  // lse2[BQ], then delta[BQ]
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE + 8 * BQ];  // Q tile, dO tile, statistics
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE + 8 * BQ];
-
   BwdTile tc;
-  if (!decode_bwd<true>(a, tc)) return;
+  if (!decode_bwd<true>(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -527,6 +545,24 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   const size_t dkidx = krow_g * a.dkv_stride + hoff;
   store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dk) + dkidx, dk, a.scale, hh);
   store_row_t<DT, D, DT32>(static_cast<uint16_t*>(a.dv) + dkidx, dv, 1.0f, hh);
+}
+
+template <int DT, int D, int NW, int BQ, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * (BQ * D * 2) + 8 * BQ];  // Q tile, dO tile, statistics
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * (BQ * D * 2) + 8 * BQ];
+  const int tasks = bwd_active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_bwd_dkdv_h16_task<DT, D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_bwd_dkdv_h16_task<DT, D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
 }
 
 }  // namespace vlp

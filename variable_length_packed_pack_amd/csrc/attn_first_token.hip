@@ -101,8 +101,9 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N],
   m = mn;
 }
 
+// One task: the wavefront's head of the sequence in tile slot `slot`.
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a, int head_groups) {
+__device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, int head) {
   using C = Chunk<DT>;
   constexpr int EPC = C::N;        // elements per 16-byte chunk
   constexpr int LPK = D / EPC;     // lanes per key row
@@ -110,12 +111,7 @@ __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a,
   constexpr int U = 4;             // steps per round
   static_assert(LPK >= 1 && LPK <= 64 && (LPK & (LPK - 1)) == 0, "lanes per key");
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int slot = static_cast<int>(blockIdx.x) / head_groups;
-  const int head = (static_cast<int>(blockIdx.x) - slot * head_groups) * 4 + wave;
-  const int g_active = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
-  if (slot >= g_active || slot >= a.grid_cap || head >= a.heads) return;  // no barriers below
+  const int lane = task_tid() & 63;
   const int f = a.tile_order ? a.tile_order[slot] : slot;
   if (f < 0 || f >= a.grid_cap) return;
   const int seq = a.grid_mapping[f];
@@ -204,37 +200,67 @@ __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a,
   }
 }
 
-template <int DT, int D>
-hipError_t launch_dt_d(const AttnArgs& a, bool causal, int64_t slots, hipStream_t s) {
+// Task t = slot * head_groups + group: wave w of the workgroup takes head
+// 4 * group + w.  One task per workgroup on the static grid; tasks
+// blockIdx.x + j * gridDim.x on the persistent grid.  Nothing is shared
+// between the waves, so there is no barrier.
+template <int DT, int D, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a, int head_groups) {
+  const int wave = threadIdx.x >> 6;
+  int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
+  g = min(g, a.grid_cap);
+  const int tasks = g > 0 ? g * head_groups : 0;
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      const int slot = task / head_groups;
+      const int head = (task - slot * head_groups) * 4 + wave;
+      if (head < a.heads) first_token_task<DT, D, CAUSAL>(a, slot, head);
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      const int slot = task / head_groups;
+      const int head = (task - slot * head_groups) * 4 + wave;
+      if (head < a.heads) first_token_task<DT, D, CAUSAL>(a, slot, head);
+    }
+  }
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_dt_d(const AttnArgs& a, int64_t slots, int32_t workers, hipStream_t s) {
   const int head_groups = (a.heads + 3) / 4;
-  const dim3 grid(static_cast<unsigned>(slots * head_groups));
-  if (causal)
-    hipLaunchKernelGGL((attn_first_token_kernel<DT, D, true>), grid, dim3(256), 0, s, a, head_groups);
-  else
-    hipLaunchKernelGGL((attn_first_token_kernel<DT, D, false>), grid, dim3(256), 0, s, a, head_groups);
+  const auto kernel = workers == kStaticGrid ? attn_first_token_kernel<DT, D, CAUSAL, false>
+                                             : attn_first_token_kernel<DT, D, CAUSAL, true>;
+  int64_t width = 0;
+  const hipError_t e = launch_width(kernel, 256, slots * head_groups, workers, &width);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(256), 0, s, a, head_groups);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, int64_t slots, hipStream_t s) {
+hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, int64_t slots, int32_t workers, hipStream_t s) {
+#define VLP_FT_CASE(D) \
+  case D: return causal ? launch_dt_d<DT, D, true>(a, slots, workers, s) : launch_dt_d<DT, D, false>(a, slots, workers, s);
   switch (head_dim) {
-    case 16: return launch_dt_d<DT, 16>(a, causal, slots, s);
-    case 32: return launch_dt_d<DT, 32>(a, causal, slots, s);
-    case 64: return launch_dt_d<DT, 64>(a, causal, slots, s);
-    case 128: return launch_dt_d<DT, 128>(a, causal, slots, s);
+    VLP_FT_CASE(16)
+    VLP_FT_CASE(32)
+    VLP_FT_CASE(64)
+    VLP_FT_CASE(128)
     default: return hipErrorInvalidValue;
   }
+#undef VLP_FT_CASE
 }
 
 }  // namespace
 
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
-                                   int64_t slots, hipStream_t s) {
+                                   int64_t slots, int32_t workers, hipStream_t s) {
   if (slots <= 0) return hipSuccess;
   switch (dtype) {
-    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, slots, s);
-    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, slots, s);
-    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, slots, s);
+    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, slots, workers, s);
+    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, slots, workers, s);
+    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, slots, workers, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,12 +7,14 @@
 // sequence in grid_mapping and processes only that sequence's tokens).
 //
 // Work decomposition ("So you wanna CUDA Graph", "Scheduling without
-// max_seqlen"): one workgroup per (tile slot, head), head fastest.  Slot s
-// runs flat tile f = tile_order[s]; seq = grid_mapping[f]; local tile
-// t = f - block_offsets[seq]; slots >= block_offsets[num_seqs] exit at once.
-// With head fastest and workgroups dealt round-robin to the 8 XCDs, a head
-// count that is a multiple of 8 keeps every tile of one (sequence, head) on
-// one XCD, so its K/V stay in that XCD's L2.
+// max_seqlen"): one task per (tile slot, head), head fastest.  Slot s runs
+// flat tile f = tile_order[s]; seq = grid_mapping[f]; local tile
+// t = f - block_offsets[seq]; tasks of slots >= block_offsets[num_seqs] are
+// not run.  A workgroup runs tasks blockIdx.x + j * gridDim.x (one task per
+// workgroup on the static grid; several on the persistent grid).  With head
+// fastest and workgroups dealt round-robin to the 8 XCDs, a head count and a
+// launch width that are multiples of 8 keep every tile of one (sequence,
+// head) on one XCD, so its K/V stay in that XCD's L2.
 //
 // Per wavefront: 32 query rows.  Per inner step: BN keys staged in LDS.
 // MFMA orientation (v_mfma_f32_32x32x16_{bf16,f16}, 64 lanes, lane = 32*hh + n):
@@ -94,18 +96,25 @@ template <> struct Half16<VLP_FP16> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Workgroup -> (sequence, local tile) through the ragged-grid metadata.
+// Task -> (sequence, local tile, head) through the ragged-grid metadata.
 struct TileCoord {
   int seq, tile, head;
   int q_start, lq, k_start, lk;
 };
 
-__device__ __forceinline__ bool decode_workgroup(const AttnArgs& a, TileCoord& tc) {
+// Active tasks of a launch: (active tile slots) * heads, the slot count
+// read on the device unless the host knows it.
+__device__ __forceinline__ int active_tasks(const AttnArgs& a) {
+  int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
+  g = min(g, a.grid_cap);
+  return g > 0 ? g * a.heads : 0;
+}
+
+// Task t (< active_tasks) is head t % heads of tile slot t / heads.
+__device__ __forceinline__ bool decode_task(const AttnArgs& a, int task, TileCoord& tc) {
   const int heads = a.heads;
-  const int slot = static_cast<int>(blockIdx.x) / heads;
-  tc.head = static_cast<int>(blockIdx.x) - slot * heads;
-  const int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
-  if (slot >= g || slot >= a.grid_cap) return false;
+  const int slot = task / heads;
+  tc.head = task - slot * heads;
   const int f = a.tile_order ? a.tile_order[slot] : slot;
   if (f < 0 || f >= a.grid_cap) return false;  // out-of-contract metadata: skip, never read past it
   tc.seq = a.grid_mapping[f];
@@ -241,8 +250,10 @@ __device__ __forceinline__ int chunk_swz(int row) {
 // s_waitcnt with only the vector-memory counter constrained (to 0).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One task (a tile of BM query rows of one head) of the 16-bit kernel.
+// lds0 and lds1 are the workgroup's two LDS buffers of 2 * BN * D * 2 bytes.
 template <int DT, int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
+__device__ __forceinline__ void attn_fwd_h16_task(const AttnArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   using E = Half16<DT>;
@@ -258,13 +269,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   constexpr int LPW = LPT / NW;        // direct loads per tile per wave
   constexpr int TILE = BN * RB;        // bytes of one K (or V) tile
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
-
   TileCoord tc;
-  if (!decode_workgroup(a, tc)) return;
+  if (!decode_task(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 31;
@@ -455,6 +463,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
     a.lse[static_cast<size_t>(tc.head) * a.rows_q + tc.q_start + my_row] =
         l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : kNegInf;
 }
+
+// Static grid (PERSISTENT false): workgroup b runs task b, if it is active.
+// Persistent grid: workgroup b runs tasks b, b + gridDim.x, ... below the
+// active count; the barrier between tasks frees both LDS buffers for the
+// next task's loads.  The two are separate instantiations so that the
+// static grid's kernel carries no loop.
+template <int DT, int D, int NW, int BN, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * BN * D * 2];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * BN * D * 2];  // buffer 1
+  const int tasks = active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_fwd_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_fwd_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs
 //
@@ -478,8 +510,9 @@ __device__ __forceinline__ int chunk_swz_f32(int row) {
   }
 }
 
+// One task of the fp32 kernel; lds0 and lds1 hold 2 * BN * D * 4 bytes each.
 template <int D, int NW, int BN, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
+__device__ __forceinline__ void attn_fwd_f32_task(const AttnArgs& a, int task, char* lds0, char* lds1) {
   static_assert(D % 16 == 0, "head_dim");
   static_assert(BN % 32 == 0, "block_n");
   constexpr int BM = 32 * NW;
@@ -494,13 +527,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   constexpr int LPW = LPT / NW;
   constexpr int TILE = BN * RB;
 
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // buffer 0: K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];  // buffer 1
-
   TileCoord tc;
-  if (!decode_workgroup(a, tc)) return;
+  if (!decode_task(a, task, tc)) return;
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -654,6 +684,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   if (a.lse && hh == 0)
     a.lse[static_cast<size_t>(tc.head) * a.rows_q + tc.q_start + my_row] =
         l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : kNegInf;
+}
+
+template <int D, int NW, int BN, bool CAUSAL, bool PERSISTENT>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * BN * D * 4];  // buffer 0: K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * BN * D * 4];  // buffer 1
+  const int tasks = active_tasks(a);
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      attn_fwd_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      attn_fwd_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+    }
+  }
 }
 
 }  // namespace vlp

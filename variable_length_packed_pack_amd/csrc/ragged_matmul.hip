@@ -12,9 +12,11 @@
 // Metadata") with 128-row tiles, times 128-column tiles of the output.  A
 // workgroup looks its row tile up in grid_mapping / block_offsets and
 // multiplies only that sequence's rows by that sequence's weight slice.
-// Workgroup b runs on XCD b % 8; the mapping below gives each XCD whole row
-// tiles, all their column tiles one after another, so a row tile of x is
-// read from HBM once per XCD and then served by that XCD's L2.
+// Workgroup b runs on XCD b % 8 and runs tasks b, b + width, ...; every
+// launch width used here is a multiple of 8, so task t runs on XCD t % 8.
+// The task mapping below gives each XCD whole row tiles, all their column
+// tiles one after another, so a row tile of x is read from HBM once per XCD
+// and then served by that XCD's L2.
 //
 // Per workgroup (4 wavefronts): output tile 128 rows x 128 columns, K in
 // stages of 64 staged in LDS (double-buffered, direct buffer-to-LDS loads
@@ -49,7 +51,7 @@ constexpr int kMmBK = 64;  // in_features per LDS stage
 // BM token rows x BN output columns per workgroup, WGM x WGN wavefronts each
 // owning (BM / WGM) tokens x (BN / WGN) columns.
 template <int DT, bool BIAS, int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged_matmul_h16(const MatmulArgs a) {
+__device__ __forceinline__ void ragged_matmul_task(const MatmulArgs& a, int task, char* lds0, char* lds1) {
   using E = Half16<DT>;
   constexpr int NW = WGM * WGN;
   constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
@@ -63,14 +65,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged
   constexpr int TW = BN * RB, TX = BM * RB;    // tile bytes
   constexpr int STAGE = TW + TX;
 
-  __shared__ __attribute__((aligned(1024))) char lds0[STAGE];  // W tile, x tile
-  __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
-
-  // Workgroup -> (row slot, column tile), XCD-aware (see the header).
-  const int b = static_cast<int>(blockIdx.x);
-  const int l = b >> 3;
+  // Task -> (row slot, column tile), XCD-aware (see the header).
+  const int l = task >> 3;
   const int nt = l % a.col_tiles;
-  const int slot = (l / a.col_tiles) * 8 + (b & 7);
+  const int slot = (l / a.col_tiles) * 8 + (task & 7);
   const int g = a.block_offsets[a.num_seqs];
   if (slot >= g || slot >= a.grid_cap) return;
   const int seq = a.grid_mapping[slot];
@@ -82,7 +80,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged
   const int n0 = nt * BN;
   const int ncols = min(BN, a.n - n0);
 
-  const int tid = threadIdx.x;
+  const int tid = task_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
@@ -204,6 +202,30 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged
   }
 }
 
+// Tasks below 8 * ceil(active slots / 8) * col_tiles run one per workgroup
+// on the static grid and as blockIdx.x + j * gridDim.x on the persistent
+// grid (a width that is a multiple of 8 keeps each row slot on the XCD its
+// tasks were dealt to).
+template <int DT, bool BIAS, int BM, int BN, int WGM, int WGN, bool PERSISTENT>
+__global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged_matmul_h16(const MatmulArgs a) {
+  constexpr int STAGE = (BN + BM) * kMmBK * 2;
+  __shared__ __attribute__((aligned(1024))) char lds0[STAGE];  // W tile, x tile
+  __shared__ __attribute__((aligned(1024))) char lds1[STAGE];
+  const int g = min(a.block_offsets[a.num_seqs], a.grid_cap);
+  const int tasks = g > 0 ? ((g + 7) & ~7) * a.col_tiles : 0;
+  if constexpr (PERSISTENT) {
+    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+      ragged_matmul_task<DT, BIAS, BM, BN, WGM, WGN>(a, task, lds0, lds1);
+      __syncthreads();
+    }
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) {
+      ragged_matmul_task<DT, BIAS, BM, BN, WGM, WGN>(a, task, lds0, lds1);
+    }
+  }
+}
+
 // Tile shape of the launch (the ragged grid's block_m is VLP_MATMUL_BLOCK_M).
 constexpr int kMmBM = VLP_MATMUL_BLOCK_M;
 constexpr int kMmBN = kMatmulBlockN;
@@ -212,25 +234,26 @@ constexpr int kMmWGN = kMatmulWavesN;
 
 namespace {
 
-template <int DT>
-hipError_t go(const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s) {
+template <int DT, bool BIAS>
+hipError_t go(const MatmulArgs& a, int64_t blocks, int32_t workers, hipStream_t s) {
   constexpr int threads = kMmWGM * kMmWGN * 64;
-  if (bias)
-    hipLaunchKernelGGL((ragged_matmul_h16<DT, true, kMmBM, kMmBN, kMmWGM, kMmWGN>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(threads), 0, s, a);
-  else
-    hipLaunchKernelGGL((ragged_matmul_h16<DT, false, kMmBM, kMmBN, kMmWGM, kMmWGN>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, a);
+  const auto kernel = workers == kStaticGrid ? ragged_matmul_h16<DT, BIAS, kMmBM, kMmBN, kMmWGM, kMmWGN, false>
+                                             : ragged_matmul_h16<DT, BIAS, kMmBM, kMmBN, kMmWGM, kMmWGN, true>;
+  int64_t width = 0;
+  const hipError_t e = launch_width(kernel, threads, blocks, workers, &width);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s) {
+hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, int32_t workers,
+                                hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   switch (dtype) {
-    case VLP_BF16: return go<VLP_BF16>(a, bias, blocks, s);
-    case VLP_FP16: return go<VLP_FP16>(a, bias, blocks, s);
+    case VLP_BF16: return bias ? go<VLP_BF16, true>(a, blocks, workers, s) : go<VLP_BF16, false>(a, blocks, workers, s);
+    case VLP_FP16: return bias ? go<VLP_FP16, true>(a, blocks, workers, s) : go<VLP_FP16, false>(a, blocks, workers, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -98,6 +98,46 @@ struct MatmulArgs {
   int64_t b_seq_stride;        // elements between sequences' biases (0: shared)
 };
 
+// Launch width of a task-looping kernel.  Every tiled kernel here runs its
+// workgroup over tasks blockIdx.x, blockIdx.x + gridDim.x, ... below the
+// active task count it reads on the device, so the same code serves both
+// schedules of "So you wanna CUDA Graph" ("Graph overcapture: bound
+// capacity-sized launches"): the static grid (one workgroup per capacity
+// task; the surplus exits at once) and the persistent grid (a fixed worker
+// count striding over the active tasks only).
+//   workers == kStaticGrid:   width = tasks.
+//   workers == kResident:     width = min(tasks, workgroups of `kernel` the
+//                             device holds at once).
+//   workers > 0:              width = min(tasks, workers).
+constexpr int32_t kStaticGrid = 0;
+constexpr int32_t kResident = -1;
+
+template <typename Kernel>
+inline hipError_t launch_width(Kernel kernel, int threads, int64_t tasks, int32_t workers, int64_t* width) {
+  *width = tasks;
+  if (workers == kStaticGrid) return hipSuccess;
+  if (workers == kResident) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    workers = per_cu > 0 && cus > 0 ? per_cu * cus : 1;
+  }
+  if (workers < *width) *width = workers;
+  return hipSuccess;
+}
+
+// threadIdx.x behind an empty asm statement.  The task functions of the
+// task-looping kernels derive their lane offsets from it, so those offsets
+// are recomputed (a few instructions) for each task instead of being hoisted
+// out of the task loop and held in registers across it.
+__device__ __forceinline__ int task_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Kernel families and their tile shapes.  block_m is the query rows per
 // workgroup tile; it is what the ragged grid is built with.
 struct TileShape {
@@ -110,25 +150,26 @@ struct TileShape {
 // the pair is not built.
 TileShape attn_tile_shape(int dtype, int head_dim);
 
-// Launch the tiled MFMA forward for `blocks` workgroups (slots * heads).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+// Launch the tiled MFMA forward over `blocks` tasks (slots * heads); the
+// launch width follows `workers` (see launch_width).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
 
 // First-token forward: one wavefront per (sequence, head), `slots` sequences.
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
-                                   int64_t slots, hipStream_t s);
+                                   int64_t slots, int32_t workers, hipStream_t s);
 
-// Backward launches, `blocks` workgroups each.
-hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, hipStream_t s);
+// Backward launches over `blocks` tasks each.
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
 
-// Ragged matrix multiplication, `blocks` workgroups.
-hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, hipStream_t s);
+// Ragged matrix multiplication over `blocks` tasks.
+hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, int32_t workers, hipStream_t s);
 
 // Document ids -> cu_seqlens with a fixed capacity (one workgroup).
 hipError_t launch_ids_to_cu(const int32_t* ids, int32_t num_tokens, int32_t max_seqs, int32_t* cu, int32_t* num_out,
