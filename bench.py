@@ -49,11 +49,11 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit tiled attention kernel (the roofline kernel of the
 # bench line); a committed HBM-traffic profile is used only while they match.
-KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_bf16.hip", "tile_config.h"]
+KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_bf16.hip", "tile_config.h", "vlp_internal.h"]
 METRIC_BWD = "varlen attn bwd TFLOP/s (2.5x forward real-token flops; % MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit dk/dv kernel (the roofline kernel of the backward line).
 KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_bf16.hip", "attn_fwd_mfma.h",
-                      "tile_config.h"]
+                      "tile_config.h", "vlp_internal.h"]
 
 
 def log(msg: str) -> None:
@@ -439,6 +439,90 @@ def bench_backward(args, wl, dev) -> int:
     return 0
 
 
+def bench_overcapture(args, wl, dev) -> int:
+    """Graph replays under overcapture ("So you wanna CUDA Graph", "Graph
+    overcapture: bound capacity-sized launches"): the forward (with
+    --backward, forward and gradients) is captured once in a HIP graph for a
+    token capacity and a sequence-slot capacity R times the workload's (the
+    tail of cu_seqlens holds zero-length sequences, the unused rows hold
+    zeros) and replayed on the workload's real lengths, under the static grid
+    (one workgroup per capacity tile and head, the surplus exiting at once)
+    and under the persistent schedule (the resident worker count striding
+    over the active tiles).  Prints one JSON line with the replay times."""
+    import torch
+
+    import variable_length_packed_pack_amd as vlp
+    import workloads
+
+    if wl.lengths_q is not None:
+        print("--overcapture runs on workloads whose query and key lengths agree", file=sys.stderr)
+        return 2
+    ratios = [float(x) for x in args.overcapture.split(",")]
+    if any(r < 1.0 for r in ratios):
+        print("--overcapture ratios must be >= 1", file=sys.stderr)
+        return 2
+    k_idx = workloads.WORKLOAD_NAMES[args.workload]
+    t, h, d, b = wl.total_tokens, wl.heads, wl.head_dim, wl.num_seqs
+    tdt = workloads.DTYPES[wl.dtype]
+    bm = vlp.kernel_block_m(tdt, d, wl.causal, False, b, t, wl.max_len)
+    dout_host = workloads.random_dout(t, h, d, wl.dtype, workloads.GRAD_SEED_BASE + k_idx) if args.backward else None
+    reps = args.steps
+    rows = []
+    for r in ratios:
+        cap_rows, cap_seqs = int(round(r * t)), int(round(r * b))
+        q, k, v = (torch.zeros(cap_rows, h, d, dtype=tdt, device=dev) for _ in range(3))
+        q[:t].copy_(wl.q.to(dev))
+        k[:t].copy_(wl.k.to(dev))
+        v[:t].copy_(wl.v.to(dev))
+        lengths = np.concatenate([wl.lengths, np.zeros(cap_seqs - b, dtype=np.int32)])
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(dev)
+        out, lse = torch.zeros_like(q), torch.zeros(h, cap_rows, device=dev)
+        ws_f = torch.empty(vlp.workspace_size(cap_seqs, cap_rows, bm), dtype=torch.uint8, device=dev)
+        if args.backward:
+            dout = torch.zeros_like(q)
+            dout[:t].copy_(dout_host.to(dev))
+            grads = tuple(torch.zeros_like(q) for _ in range(3))
+            ws_b = torch.empty(vlp.bwd_workspace_size(cap_seqs, cap_rows, cap_rows, h, bm), dtype=torch.uint8,
+                               device=dev)
+        rec = {"capacity_ratio": r, "capacity_tokens": cap_rows, "capacity_seqs": cap_seqs,
+               "capacity_tiles": vlp.grid_capacity(cap_rows, cap_seqs, bm),
+               "active_tiles": int(np.sum((wl.lengths.astype(np.int64) + bm - 1) // bm))}
+        for name, nw in (("static", None), ("persistent", 0)):
+            def step():
+                vlp.varlen_attn_fwd(q, k, v, cu, cu, 0, wl.scale, wl.causal, False, out=out, lse=lse, workspace=ws_f,
+                                    num_workers=nw)
+                if args.backward:
+                    vlp.varlen_attn_bwd(q, k, v, out, dout, lse, cu, cu, 0, wl.scale, wl.causal, *grads,
+                                        workspace=ws_b, num_workers=nw)
+            step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            for _ in range(max(args.warmup, 1)):
+                graph.replay()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(reps):
+                graph.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            rec[f"{name}_ms"] = round(ev0.elapsed_time(ev1) / reps, 4)
+            del graph
+        log(f"[bench] overcapture x{r:g}: static {rec['static_ms']:.4f} ms, persistent {rec['persistent_ms']:.4f} ms")
+        rows.append(rec)
+        del q, k, v, out, lse, ws_f
+        if args.backward:
+            del dout, grads, ws_b
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "overcapture", "workload": wl.name, "dtype": wl.dtype,
+                      "pass": "forward+backward" if args.backward else "forward", "replays": reps,
+                      "num_seqs": b, "total_tokens": t, "heads": h, "head_dim": d, "causal": wl.causal,
+                      "block_m": bm, "rows": rows}), flush=True)
+    return 0
+
+
 def bench_matmul(args, wl, dev) -> int:
     """Ragged matrix multiplication on the workload's token split: the packed
     QKV projection (hidden = heads x head_dim -> 3 x hidden, one shared
@@ -570,6 +654,9 @@ def main() -> int:
                     help="measure the gradients (dq, dk, dv) instead of the forward")
     ap.add_argument("--matmul", choices=["shared", "per-seq"], default=None,
                     help="measure the ragged matrix multiplication on the workload's token split instead")
+    ap.add_argument("--overcapture", default=None, metavar="R1,R2,...",
+                    help="graph replays captured for R times the workload's token and sequence capacity, "
+                         "static grid against persistent schedule (with --backward: forward and gradients)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
                          "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -604,6 +691,8 @@ def main() -> int:
     wl = workloads.make_workload(k_idx)
     if args.matmul:
         return bench_matmul(args, wl, dev)
+    if args.overcapture:
+        return bench_overcapture(args, wl, dev)
     if args.backward:
         if args.first_token:
             print("--backward has no first-token mode", file=sys.stderr)

@@ -162,9 +162,10 @@ int32_t vlp_kernel_block_m(int32_t dtype, int32_t head_dim, int32_t causal,
 
 /*
  * vlp_varlen_attn_workspace_size -- bytes of device workspace that
- * vlp_varlen_attn_fwd needs for the device-built grid (block_offsets,
- * grid_mapping, tile_order for G_cap(rows, num_seqs, block_m) tiles, where
- * rows = rows_q, or num_seqs in first-token mode).
+ * vlp_varlen_attn_fwd(_persistent) needs for the device-built grid
+ * (block_offsets, grid_mapping, tile_order for G_cap(rows, num_seqs,
+ * block_m) tiles, where rows = rows_q, or num_seqs in first-token mode) and
+ * the persistent schedule's work-queue counters.
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, block_m < 1
  * -> VLP_ERR_INVALID.
  */
@@ -274,16 +275,20 @@ vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k,
  * schedule of "So you wanna CUDA Graph" ("Graph overcapture: bound
  * capacity-sized launches"): instead of one workgroup per capacity task
  * (G_cap(rows_q, num_seqs, block_m) * heads, the surplus exiting at once),
- * min(capacity tasks, W) workgroups are launched and each strides over the
- * ACTIVE tasks (block_offsets[num_seqs] * heads, read on the device), so a
- * launch recorded for a large token capacity costs what the real tokens
- * need.  Every argument means what it means for vlp_varlen_attn_fwd, and
- * the results are bit-identical to it (each task computes the same values).
+ * min(capacity tasks, W) workgroups are launched and they take the ACTIVE
+ * tasks (block_offsets[num_seqs] * heads, read on the device) from work
+ * queues in device memory (one per XCD, in longest-first order, cleared by
+ * the grid build that precedes the launch), so a launch recorded for a large
+ * token capacity launches no more workgroups than the device holds.  Every
+ * argument means what it means for vlp_varlen_attn_fwd (the workspace also
+ * holds the queue counters: calls that share a workspace must not overlap),
+ * and the results are bit-identical to it (each task computes the same
+ * values).
  *
  *   num_workers    W; 0 = the number of workgroups of the kernel the device
  *                  holds at once (compute units x workgroups per unit);
- *                  > 0 = at most that many (a multiple of 8 keeps a
- *                  sequence's tiles on one XCD's L2).
+ *                  > 0 = at most that many (8 or more keep every task on
+ *                  the XCD the static grid would run it on).
  * Errors: as vlp_varlen_attn_fwd, plus num_workers < 0 -> VLP_ERR_INVALID.
  */
 vlp_status vlp_varlen_attn_fwd_persistent(int32_t dtype, const void* q, const void* k, const void* v,
@@ -304,11 +309,11 @@ vlp_status vlp_varlen_attn_fwd_persistent(int32_t dtype, const void* q, const vo
 
 /*
  * vlp_varlen_attn_bwd_workspace_size -- bytes of device workspace that
- * vlp_varlen_attn_bwd needs: two fp32 [heads, rows_q] row statistics plus a
- * device-built grid over the query lengths and one over the key lengths
- * (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k, num_seqs,
- * VLP_BWD_BLOCK_K) tiles), block_m = vlp_kernel_block_m(dtype, head_dim,
- * causal, 0, ...).
+ * vlp_varlen_attn_bwd(_persistent) needs: two fp32 [heads, rows_q] row
+ * statistics plus a device-built grid over the query lengths and one over
+ * the key lengths (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k,
+ * num_seqs, VLP_BWD_BLOCK_K) tiles, each with its work-queue counters),
+ * block_m = vlp_kernel_block_m(dtype, head_dim, causal, 0, ...).
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, total_k < 0,
  * heads < 1, block_m < 1 -> VLP_ERR_INVALID; rows beyond int32 ->
  * VLP_ERR_OVERFLOW.
@@ -369,8 +374,8 @@ vlp_status vlp_varlen_attn_bwd(int32_t dtype, const void* q, const void* k, cons
 /*
  * vlp_varlen_attn_bwd_persistent -- vlp_varlen_attn_bwd with the persistent
  * schedule (see vlp_varlen_attn_fwd_persistent): each of the two gradient
- * launches has min(its capacity tasks, W) workgroups striding over its
- * active tasks.  Arguments and results (bit-identical) as for
+ * launches has min(its capacity tasks, W) workgroups taking its active
+ * tasks from its own work queues.  Arguments and results (bit-identical) as for
  * vlp_varlen_attn_bwd; num_workers as for vlp_varlen_attn_fwd_persistent,
  * W counted per launch.
  * Errors: as vlp_varlen_attn_bwd, plus num_workers < 0 -> VLP_ERR_INVALID.
@@ -436,8 +441,8 @@ vlp_status vlp_varlen_attn_bwd_grid(int32_t dtype, const void* q, const void* k,
 
 /*
  * vlp_ragged_matmul_workspace_size -- bytes of device workspace that
- * vlp_ragged_matmul needs (its device-built grid: G_cap(rows, num_seqs,
- * VLP_MATMUL_BLOCK_M) tiles).
+ * vlp_ragged_matmul(_persistent) needs (its device-built grid: G_cap(rows,
+ * num_seqs, VLP_MATMUL_BLOCK_M) tiles, and work-queue counters).
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows < 0 ->
  * VLP_ERR_INVALID.
  */
@@ -490,8 +495,8 @@ vlp_status vlp_ragged_matmul(int32_t dtype, const void* x, const void* weight, c
 /*
  * vlp_ragged_matmul_persistent -- vlp_ragged_matmul with the persistent
  * schedule (see vlp_varlen_attn_fwd_persistent): min(capacity tasks, W)
- * workgroups stride over the (row tile, column tile) tasks of the active
- * rows.  Arguments and results (bit-identical) as for vlp_ragged_matmul;
+ * workgroups take the (row tile, column tile) tasks of the active rows from
+ * work queues.  Arguments and results (bit-identical) as for vlp_ragged_matmul;
  * num_workers as for vlp_varlen_attn_fwd_persistent.
  * Errors: as vlp_ragged_matmul, plus num_workers < 0 -> VLP_ERR_INVALID.
  */

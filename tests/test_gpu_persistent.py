@@ -265,3 +265,34 @@ def test_graph_replays_follow_the_active_lengths():
         assert _same(got[0][:t], ref_out[:t]) and _same(got[1][:, :t], ref_lse[:, :t])
         for a, b in zip(got[2:], ref_g):
             assert _same(a[:t], b[:t])
+
+
+@pytest.mark.parametrize("workers", [1, 5, 8, 13, 0])
+def test_every_task_runs_exactly_once(workers):
+    """Every task of a persistent launch makes one claim on its queue, so the
+    queue counters (in the workspace, after the three grid arrays, one
+    256-byte line each) end at the number of tasks of each queue; together
+    with the bitwise checks above, every active task ran exactly once and no
+    capacity task ran at all."""
+    lengths = [100, 37, 1, 250, 64, 0, 0]
+    heads, head_dim, dtype = 8, 128, "bf16"
+    tdt = workloads.DTYPES[dtype]
+    bm = vlp.kernel_block_m(tdt, head_dim, True, False, len(lengths), 0, 0)
+    b, t = len(lengths), int(sum(lengths))
+    cap_rows = 4 * t
+    wl, (q, k, v), cu, _ = _capacity_inputs(lengths[:5], cap_rows, b, heads, head_dim, dtype, 38)
+    ws = torch.zeros(vlp.workspace_size(b, cap_rows, bm), dtype=torch.uint8, device=DEV)
+    vlp.varlen_attn_fwd(q, k, v, cu, cu, 0, None, True, False, workspace=ws, num_workers=workers)
+    torch.cuda.synchronize()
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    cap = vlp.grid_capacity(cap_rows, b, bm)
+    off = up(4 * (b + 1)) + 2 * up(4 * cap)
+    counters = ws[off:off + 8 * 256].cpu().view(torch.int32)[::64].tolist()
+    tasks = sum((n + bm - 1) // bm for n in lengths) * heads
+    width = cap * heads if workers == 0 else min(cap * heads, workers)  # the resident count is >= 8
+    nq = min(8, width)
+    expect = [len(range(x, tasks, nq)) if x < nq else 0 for x in range(8)]
+    _say(f"[persistent] workers={workers}: queue counters {counters}, expected {expect}")
+    assert counters == expect

@@ -189,7 +189,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     device) to skip the device grid build.  ``num_workers``: None launches
     the static grid (one workgroup per capacity tile and head); an int
     launches the persistent schedule with that many workgroups at most (0 =
-    as many as the device holds at once), striding over the active tiles.
+    as many as the device holds at once), which take the active tiles from
+    work queues.
     """
     lib = _lib.load()
     if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens_k.is_cuda):

@@ -28,9 +28,10 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout of the device-built grid: [block_offsets | grid_mapping |
-// tile_order], each 256-byte aligned.
+// tile_order | work-queue counters of a persistent launch], each 256-byte
+// aligned.
 struct GridWorkspace {
-  size_t off_bo, off_gm, off_to, bytes;
+  size_t off_bo, off_gm, off_to, off_ctr, bytes;
 };
 
 GridWorkspace grid_workspace(int32_t num_seqs, int64_t cap) {
@@ -38,7 +39,8 @@ GridWorkspace grid_workspace(int32_t num_seqs, int64_t cap) {
   w.off_bo = 0;
   w.off_gm = round_up(sizeof(int32_t) * (static_cast<size_t>(num_seqs) + 1), 256);
   w.off_to = w.off_gm + round_up(sizeof(int32_t) * static_cast<size_t>(cap), 256);
-  w.bytes = w.off_to + round_up(sizeof(int32_t) * static_cast<size_t>(cap), 256);
+  w.off_ctr = w.off_to + round_up(sizeof(int32_t) * static_cast<size_t>(cap), 256);
+  w.bytes = w.off_ctr + sizeof(int32_t) * vlp::kTaskQueues * vlp::kCounterStride;
   return w;
 }
 
@@ -211,7 +213,7 @@ extern "C" vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, in
   if (!cu_seqlens || !block_offsets || !grid_mapping || !tile_order) return VLP_ERR_NULL;
   if (num_seqs < 1 || block_m < 1 || grid_cap < 0 || grid_cap > INT32_MAX) return VLP_ERR_INVALID;
   return hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, block_m, block_offsets, grid_mapping, tile_order,
-                                           grid_cap, static_cast<hipStream_t>(stream)));
+                                           grid_cap, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -239,12 +241,14 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   int32_t* bo = reinterpret_cast<int32_t*>(base + w.off_bo);
   int32_t* gm = reinterpret_cast<int32_t*>(base + w.off_gm);
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
+  int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t* grid_cu = query_is_first_token ? cu_seqlens_k : cu_seqlens_q;
-  st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, s));
+  st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, ctr, s));
   if (st != VLP_OK) return st;
 
   vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse, c);
+  a.task_counter = ctr;
   a.grid_mapping = gm;
   a.block_offsets = bo;
   a.tile_order = to;
@@ -430,8 +434,10 @@ vlp_status bwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
     int32_t* bo = reinterpret_cast<int32_t*>(g + w.qg.off_bo);
     int32_t* gm = reinterpret_cast<int32_t*>(g + w.qg.off_gm);
     int32_t* to = reinterpret_cast<int32_t*>(g + w.qg.off_to);
-    st = hip_status(vlp::launch_grid_build(cu_seqlens_q, num_seqs, c.block_m, bo, gm, to, w.cap_q, s));
+    int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(g + w.qg.off_ctr);
+    st = hip_status(vlp::launch_grid_build(cu_seqlens_q, num_seqs, c.block_m, bo, gm, to, w.cap_q, ctr, s));
     if (st != VLP_OK) return st;
+    a.task_counter = ctr;
     a.grid_mapping = gm;
     a.block_offsets = bo;
     a.tile_order = to;
@@ -444,8 +450,10 @@ vlp_status bwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
     int32_t* bo = reinterpret_cast<int32_t*>(g + w.kg.off_bo);
     int32_t* gm = reinterpret_cast<int32_t*>(g + w.kg.off_gm);
     int32_t* to = reinterpret_cast<int32_t*>(g + w.kg.off_to);
-    st = hip_status(vlp::launch_grid_build(cu_seqlens_k, num_seqs, VLP_BWD_BLOCK_K, bo, gm, to, w.cap_k, s));
+    int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(g + w.kg.off_ctr);
+    st = hip_status(vlp::launch_grid_build(cu_seqlens_k, num_seqs, VLP_BWD_BLOCK_K, bo, gm, to, w.cap_k, ctr, s));
     if (st != VLP_OK) return st;
+    a.task_counter = ctr;
     a.grid_mapping = gm;
     a.block_offsets = bo;
     a.tile_order = to;
@@ -571,10 +579,13 @@ vlp_status matmul_device_grid(int32_t dtype, const void* x, const void* weight, 
   int32_t* bo = reinterpret_cast<int32_t*>(base + w.off_bo);
   int32_t* gm = reinterpret_cast<int32_t*>(base + w.off_gm);
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
+  int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  vlp_status st = hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, VLP_MATMUL_BLOCK_M, bo, gm, to, cap, s));
+  vlp_status st =
+      hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, VLP_MATMUL_BLOCK_M, bo, gm, to, cap, ctr, s));
   if (st != VLP_OK) return st;
   vlp::MatmulArgs a{};
+  a.task_counter = ctr;
   a.x = x;
   a.w = weight;
   a.bias = bias;

@@ -244,10 +244,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds1[2 * (BN * D * 4)];  // buffer 1
   const int tasks = bwd_active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_bwd_dq_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {
@@ -427,10 +427,10 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   __shared__ __attribute__((aligned(1024))) char lds1[2 * (BQ * D * 4) + 8 * kStatRows];
   const int tasks = bwd_active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_bwd_dkdv_f32_task<D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {

@@ -54,8 +54,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Task -> (sequence, local tile, head) for a backward launch.  KEY_GRID: the
 // grid was built over the key lengths, and local tiles run in mirrored order.
 // Tasks are laid out as in the forward (head fastest) and run as there: one
-// per workgroup on the static grid, blockIdx.x + j * gridDim.x on the
-// persistent grid.
+// per workgroup on the static grid, from the work queues on the persistent
+// grid.
 struct BwdTile {
   int seq, tile, head;
   int q_start, lq, k_start, lk;
@@ -369,10 +369,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds1[2 * (BN * D * 2)];  // buffer 1
   const int tasks = bwd_active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_bwd_dq_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {
@@ -553,10 +553,10 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   __shared__ __attribute__((aligned(1024))) char lds1[2 * (BQ * D * 2) + 8 * BQ];
   const int tasks = bwd_active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_bwd_dkdv_h16_task<DT, D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {

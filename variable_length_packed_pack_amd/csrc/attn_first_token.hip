@@ -201,9 +201,8 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
 }
 
 // Task t = slot * head_groups + group: wave w of the workgroup takes head
-// 4 * group + w.  One task per workgroup on the static grid; tasks
-// blockIdx.x + j * gridDim.x on the persistent grid.  Nothing is shared
-// between the waves, so there is no barrier.
+// 4 * group + w.  One task per workgroup on the static grid; tasks from the
+// work queues on the persistent grid.
 template <int DT, int D, bool CAUSAL, bool PERSISTENT>
 __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a, int head_groups) {
   const int wave = threadIdx.x >> 6;
@@ -211,11 +210,12 @@ __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a,
   g = min(g, a.grid_cap);
   const int tasks = g > 0 ? g * head_groups : 0;
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    __shared__ int mailbox;
+    run_claimed_tasks(tasks, a.task_counter, &mailbox, [&](int task) __attribute__((always_inline)) {
       const int slot = task / head_groups;
       const int head = (task - slot * head_groups) * 4 + wave;
       if (head < a.heads) first_token_task<DT, D, CAUSAL>(a, slot, head);
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {
@@ -240,8 +240,10 @@ hipError_t launch_dt_d(const AttnArgs& a, int64_t slots, int32_t workers, hipStr
 
 template <int DT>
 hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, int64_t slots, int32_t workers, hipStream_t s) {
-#define VLP_FT_CASE(D) \
-  case D: return causal ? launch_dt_d<DT, D, true>(a, slots, workers, s) : launch_dt_d<DT, D, false>(a, slots, workers, s);
+#define VLP_FT_CASE(D)                                                         \
+  case D:                                                                      \
+    return causal ? launch_dt_d<DT, D, true>(a, slots, workers, s)             \
+                  : launch_dt_d<DT, D, false>(a, slots, workers, s);
   switch (head_dim) {
     VLP_FT_CASE(16)
     VLP_FT_CASE(32)

@@ -10,11 +10,12 @@
 // max_seqlen"): one task per (tile slot, head), head fastest.  Slot s runs
 // flat tile f = tile_order[s]; seq = grid_mapping[f]; local tile
 // t = f - block_offsets[seq]; tasks of slots >= block_offsets[num_seqs] are
-// not run.  A workgroup runs tasks blockIdx.x + j * gridDim.x (one task per
-// workgroup on the static grid; several on the persistent grid).  With head
-// fastest and workgroups dealt round-robin to the 8 XCDs, a head count and a
-// launch width that are multiples of 8 keep every tile of one (sequence,
-// head) on one XCD, so its K/V stay in that XCD's L2.
+// not run.  On the static grid workgroup b runs task b; on the persistent
+// grid a fixed worker count takes the tasks from per-XCD work queues that
+// keep task t on XCD t % 8 (run_claimed_tasks).  With head fastest and
+// workgroups dealt round-robin to the 8 XCDs, a head count that is a
+// multiple of 8 keeps every tile of one (sequence, head) on one XCD, so its
+// K/V stay in that XCD's L2.
 //
 // Per wavefront: 32 query rows.  Per inner step: BN keys staged in LDS.
 // MFMA orientation (v_mfma_f32_32x32x16_{bf16,f16}, 64 lanes, lane = 32*hh + n):
@@ -465,20 +466,19 @@ __device__ __forceinline__ void attn_fwd_h16_task(const AttnArgs& a, int task, c
 }
 
 // Static grid (PERSISTENT false): workgroup b runs task b, if it is active.
-// Persistent grid: workgroup b runs tasks b, b + gridDim.x, ... below the
-// active count; the barrier between tasks frees both LDS buffers for the
-// next task's loads.  The two are separate instantiations so that the
-// static grid's kernel carries no loop.
+// Persistent grid: the workgroup runs the tasks it takes from the work
+// queues (run_claimed_tasks).  The two are separate instantiations so that
+// the static grid's kernel carries no loop.
 template <int DT, int D, int NW, int BN, bool CAUSAL, bool PERSISTENT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds0[2 * BN * D * 2];  // buffer 0: K tile, V tile
   __shared__ __attribute__((aligned(1024))) char lds1[2 * BN * D * 2];  // buffer 1
   const int tasks = active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_fwd_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {
@@ -692,10 +692,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds1[2 * BN * D * 4];  // buffer 1
   const int tasks = active_tasks(a);
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       attn_fwd_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {

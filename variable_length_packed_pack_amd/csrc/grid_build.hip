@@ -12,13 +12,17 @@
 //      waves) -> block_offsets; grid_mapping one tile per thread, by a
 //      binary search of the offsets;
 //   2. longest-first order (length descending, ties to the lower index, the
-//      order of a stable sort by length): for up to kRankMax sequences every
-//      sequence counts the sequences that precede it; above that, a bitonic
-//      sort in LDS of the keys ((INT32_MAX - len) << 32 | i);
+//      order of a stable sort by length) of the M non-empty sequences only:
+//      they are compacted first (a scan of the non-empty flags), so a launch
+//      sized for a sequence capacity far above M -- a zero-length tail of
+//      capacity slots -- orders M keys, not the capacity.  For up to kRankMax
+//      of them every sequence counts the sequences that precede it; above
+//      that, a bitonic sort in LDS of the keys ((INT32_MAX - len) << 32 | i);
 //   3. a second prefix sum of tile counts in that order gives every
 //      sequence's position in tile_order; each slot is filled by its own
 //      thread (binary search of the positions), last tile first.
-// Entries from G to grid_cap are set to -1.
+// Entries from G to grid_cap are set to -1.  The kernel also clears the
+// work-queue counters of the persistent launch that follows it, if given.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,7 +67,8 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
 __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __restrict__ cu, int num_seqs,
                                                               int block_m, int32_t* __restrict__ block_offsets,
                                                               int32_t* __restrict__ grid_mapping,
-                                                              int32_t* __restrict__ tile_order, int grid_cap) {
+                                                              int32_t* __restrict__ tile_order, int grid_cap,
+                                                              int32_t* __restrict__ task_counter) {
   __shared__ int len_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int bo_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int order_s[VLP_DEVICE_SORT_MAX_SEQS];
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
   const int beg = min(num_seqs, tid * per);
   const int end = min(num_seqs, beg + per);
   const bool sorted = num_seqs <= VLP_DEVICE_SORT_MAX_SEQS;
+  if (task_counter && tid < kTaskQueues) task_counter[tid * kCounterStride] = 0;
 
   // 1. block_offsets and grid_mapping.
   int local = 0;
@@ -123,12 +129,23 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
     grid_mapping[f] = owner;
   }
 
-  // 2. the longest-first order: order_s[r] = the sequence at rank r.
-  if (num_seqs <= kRankMax) {
-    for (int i = tid; i < num_seqs; i += kThreads) {
+  // 2. the longest-first order of the non-empty sequences: order_s[r] = the
+  // sequence at rank r < m.  pos_s first holds the compacted list of
+  // non-empty sequences, in index order.
+  local = 0;
+  for (int i = beg; i < end; ++i) local += len_s[i] > 0;
+  int m = 0;
+  int at = block_exclusive_scan(local, wave_sums, &m);
+  for (int i = beg; i < end; ++i)
+    if (len_s[i] > 0) pos_s[at++] = i;
+  __syncthreads();
+  if (m <= kRankMax) {
+    for (int a = tid; a < m; a += kThreads) {
+      const int i = pos_s[a];
       const int li = len_s[i];
       int rank = 0;
-      for (int j = 0; j < num_seqs; ++j) {
+      for (int b = 0; b < m; ++b) {
+        const int j = pos_s[b];
         const int lj = len_s[j];
         rank += (lj > li) || (lj == li && j < i);
       }
@@ -136,13 +153,14 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
     }
   } else {
     int p2 = 1;
-    while (p2 < num_seqs) p2 <<= 1;
-    for (int i = tid; i < p2; i += kThreads) {
-      if (i < num_seqs) {
+    while (p2 < m) p2 <<= 1;
+    for (int a = tid; a < p2; a += kThreads) {
+      if (a < m) {
+        const int i = pos_s[a];
         const unsigned len = static_cast<unsigned>(len_s[i]);
-        keys[i] = (static_cast<unsigned long long>(0x7fffffffu - len) << 32) | static_cast<unsigned>(i);
+        keys[a] = (static_cast<unsigned long long>(0x7fffffffu - len) << 32) | static_cast<unsigned>(i);
       } else {
-        keys[i] = ~0ull;
+        keys[a] = ~0ull;
       }
     }
     __syncthreads();
@@ -162,25 +180,28 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
         __syncthreads();
       }
     }
-    for (int r = tid; r < num_seqs; r += kThreads) order_s[r] = static_cast<int>(keys[r] & 0xffffffffu);
+    for (int r = tid; r < m; r += kThreads) order_s[r] = static_cast<int>(keys[r] & 0xffffffffu);
   }
-  __syncthreads();
+  __syncthreads();  // order_s complete; pos_s free again
 
   // 3. positions in the longest-first order (pos_s[r] = first slot of the
   // sequence at rank r), then one slot per thread: slot p belongs to the
   // last rank whose position is <= p and takes that sequence's tiles from
   // its last local tile down to tile 0.
+  const int rper = (m + kThreads - 1) / kThreads;
+  const int rbeg = min(m, tid * rper);
+  const int rend = min(m, rbeg + rper);
   local = 0;
-  for (int r = beg; r < end; ++r) local += tiles_for(len_s[order_s[r]], block_m);
+  for (int r = rbeg; r < rend; ++r) local += tiles_for(len_s[order_s[r]], block_m);
   int dummy = 0;
   int pos = block_exclusive_scan(local, wave_sums, &dummy);
-  for (int r = beg; r < end; ++r) {
+  for (int r = rbeg; r < rend; ++r) {
     pos_s[r] = pos;
     pos += tiles_for(len_s[order_s[r]], block_m);
   }
   __syncthreads();
   for (int p = tid; p < gw; p += kThreads) {
-    int lo = 0, hi = num_seqs - 1;  // pos_s[0] = 0 <= p
+    int lo = 0, hi = m - 1;  // pos_s[0] = 0 <= p (p < gw implies m >= 1)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pos_s[mid] <= p) lo = mid; else hi = mid - 1;
@@ -196,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
 
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                              int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
-                             int64_t grid_cap, hipStream_t s) {
+                             int64_t grid_cap, int32_t* task_counter, hipStream_t s) {
   hipLaunchKernelGGL(grid_build_kernel, dim3(1), dim3(kThreads), 0, s, cu_seqlens, num_seqs, block_m,
-                     block_offsets, grid_mapping, tile_order, static_cast<int>(grid_cap));
+                     block_offsets, grid_mapping, tile_order, static_cast<int>(grid_cap), task_counter);
   return hipGetLastError();
 }
 

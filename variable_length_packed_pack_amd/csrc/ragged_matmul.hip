@@ -12,11 +12,11 @@
 // Metadata") with 128-row tiles, times 128-column tiles of the output.  A
 // workgroup looks its row tile up in grid_mapping / block_offsets and
 // multiplies only that sequence's rows by that sequence's weight slice.
-// Workgroup b runs on XCD b % 8 and runs tasks b, b + width, ...; every
-// launch width used here is a multiple of 8, so task t runs on XCD t % 8.
-// The task mapping below gives each XCD whole row tiles, all their column
-// tiles one after another, so a row tile of x is read from HBM once per XCD
-// and then served by that XCD's L2.
+// Task t runs on XCD t % 8 (static grid: workgroup t, dealt round-robin to
+// the XCDs; persistent grid: the per-XCD work queues).  The task mapping
+// below gives each XCD whole row tiles, all their column tiles one after
+// another, so a row tile of x is read from HBM once per XCD and then served
+// by that XCD's L2.
 //
 // Per workgroup (4 wavefronts): output tile 128 rows x 128 columns, K in
 // stages of 64 staged in LDS (double-buffered, direct buffer-to-LDS loads
@@ -203,9 +203,7 @@ __device__ __forceinline__ void ragged_matmul_task(const MatmulArgs& a, int task
 }
 
 // Tasks below 8 * ceil(active slots / 8) * col_tiles run one per workgroup
-// on the static grid and as blockIdx.x + j * gridDim.x on the persistent
-// grid (a width that is a multiple of 8 keeps each row slot on the XCD its
-// tasks were dealt to).
+// on the static grid and from the work queues on the persistent grid.
 template <int DT, bool BIAS, int BM, int BN, int WGM, int WGN, bool PERSISTENT>
 __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged_matmul_h16(const MatmulArgs a) {
   constexpr int STAGE = (BN + BM) * kMmBK * 2;
@@ -214,10 +212,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged
   const int g = min(a.block_offsets[a.num_seqs], a.grid_cap);
   const int tasks = g > 0 ? ((g + 7) & ~7) * a.col_tiles : 0;
   if constexpr (PERSISTENT) {
-    for (int task = blockIdx.x; task < tasks; task += gridDim.x) {
+    int* mailbox = reinterpret_cast<int*>(lds0);
+    run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
       ragged_matmul_task<DT, BIAS, BM, BN, WGM, WGN>(a, task, lds0, lds1);
-      __syncthreads();
-    }
+    });
   } else {
     const int task = blockIdx.x;
     if (task < tasks) {

@@ -37,6 +37,7 @@ struct AttnArgs {
   int32_t q_stride;
   int32_t kv_stride;           // k and v
   int32_t o_stride;
+  int32_t* task_counter;       // persistent launches: the queue counters (zero at launch)
 };
 
 // Arguments of the two backward launches (the dQ kernel over the query
@@ -71,6 +72,7 @@ struct BwdArgs {
   int32_t do_stride;           // dout
   int32_t dq_stride;
   int32_t dkv_stride;          // dk and dv
+  int32_t* task_counter;       // persistent launches: the queue counters (zero at launch)
 };
 
 // Ragged matrix multiplication tiles: VLP_MATMUL_BLOCK_M token rows x
@@ -96,19 +98,16 @@ struct MatmulArgs {
   int32_t col_tiles;           // ceil(n / kMatmulBlockN)
   int64_t w_seq_stride;        // elements between sequences' weights (0: shared)
   int64_t b_seq_stride;        // elements between sequences' biases (0: shared)
+  int32_t* task_counter;       // persistent launches: the queue counters (zero at launch)
 };
 
-// Launch width of a task-looping kernel.  Every tiled kernel here runs its
-// workgroup over tasks blockIdx.x, blockIdx.x + gridDim.x, ... below the
-// active task count it reads on the device, so the same code serves both
-// schedules of "So you wanna CUDA Graph" ("Graph overcapture: bound
-// capacity-sized launches"): the static grid (one workgroup per capacity
-// task; the surplus exits at once) and the persistent grid (a fixed worker
-// count striding over the active tasks only).
-//   workers == kStaticGrid:   width = tasks.
-//   workers == kResident:     width = min(tasks, workgroups of `kernel` the
-//                             device holds at once).
-//   workers > 0:              width = min(tasks, workers).
+// Launch width of a kernel over `tasks` tasks, for the two schedules of "So
+// you wanna CUDA Graph" ("Graph overcapture: bound capacity-sized
+// launches").  Static grid (workers == kStaticGrid): one workgroup per
+// capacity task; tasks past the active count, read on the device, exit at
+// once.  Persistent grid: a fixed worker count (kResident: as many
+// workgroups of `kernel` as the device holds at once; > 0: at most that
+// many) that takes the active tasks from a work queue (run_claimed_tasks).
 constexpr int32_t kStaticGrid = 0;
 constexpr int32_t kResident = -1;
 
@@ -126,6 +125,53 @@ inline hipError_t launch_width(Kernel kernel, int threads, int64_t tasks, int32_
   }
   if (workers < *width) *width = workers;
   return hipSuccess;
+}
+
+// Persistent workgroups take the active tasks from work queues, one per XCD
+// (nq = 8 of them; fewer, one per workgroup, when fewer than 8 workgroups
+// run).  The hardware deals workgroup b to XCD b % 8 and, on the static
+// grid, starts each XCD's workgroups in order; the queues do the same for
+// the persistent grid: queue x holds the tasks t = x + nq*i in order of i,
+// its first n_x tasks go to the n_x workgroups b = x + nq*i launched on XCD
+// x, and each later one to the workgroup that claims it from counter[x] (a
+// 256-byte line of its own, zero when the launch starts: the grid build
+// that precedes every persistent launch on its stream clears it), as
+// i = n_x + the counter's previous value.  A workgroup stops at its first
+// claim past `tasks`, so every task runs exactly once and counter[x] ends at
+// the number of tasks in queue x.  The longest-first order of the task list
+// and the XCD a task's K/V (or rows of x) are cached on are what they are on
+// the static grid.
+//   The claim for the next task is issued as the current task starts, so
+// its latency hides behind the task.  `mailbox` is an int in the kernel's
+// own LDS (the first word of a tile buffer, so the persistent kernel needs
+// no more LDS, and no lower occupancy, than the static one): between two
+// tasks, with every wave past the task's LDS use, thread 0 posts the claim
+// there, and every wave reads it before any wave starts the next task.  The
+// task index is made wave-uniform, so the task's address arithmetic stays
+// scalar.
+constexpr int kTaskQueues = 8;
+// Elements between two queue counters: one 256-byte line each.  Atomics on
+// one line are serialised device-wide (about 10 ns apiece when every
+// workgroup claims at once); on separate lines they proceed in parallel.
+constexpr int kCounterStride = 64;
+
+template <typename Fn>
+__device__ __forceinline__ void run_claimed_tasks(int tasks, int32_t* counters, int* mailbox, Fn&& fn) {
+  const int w = static_cast<int>(gridDim.x);
+  const int nq = w < kTaskQueues ? w : kTaskQueues;  // every queue needs a worker
+  const int x = static_cast<int>(blockIdx.x) % nq;
+  const int n_x = (w - x + nq - 1) / nq;
+  int task = static_cast<int>(blockIdx.x);
+  while (task < tasks) {
+    int claimed = 0;
+    if (threadIdx.x == 0) claimed = atomicAdd(counters + x * kCounterStride, 1);
+    fn(task);
+    __syncthreads();  // the task's LDS traffic is over
+    if (threadIdx.x == 0) *mailbox = x + nq * (n_x + claimed);
+    __syncthreads();  // the claim is posted
+    task = __builtin_amdgcn_readfirstlane(*mailbox);
+    __syncthreads();  // and read by every wave before the LDS is reused
+  }
 }
 
 // threadIdx.x behind an empty asm statement.  The task functions of the
@@ -152,32 +198,44 @@ TileShape attn_tile_shape(int dtype, int head_dim);
 
 // Launch the tiled MFMA forward over `blocks` tasks (slots * heads); the
 // launch width follows `workers` (see launch_width).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks,
+                            int32_t workers, hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t blocks,
+                           int32_t workers, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks,
+                           int32_t workers, hipStream_t s);
 
 // First-token forward: one wavefront per (sequence, head), `slots` sequences.
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
                                    int64_t slots, int32_t workers, hipStream_t s);
 
 // Backward launches over `blocks` tasks each.
-hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
-hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                   int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                     int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                  int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                    int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                  int32_t workers, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
+                                    int32_t workers, hipStream_t s);
 
 // Ragged matrix multiplication over `blocks` tasks.
-hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks, int32_t workers, hipStream_t s);
+hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks,
+                                int32_t workers, hipStream_t s);
 
 // Document ids -> cu_seqlens with a fixed capacity (one workgroup).
 hipError_t launch_ids_to_cu(const int32_t* ids, int32_t num_tokens, int32_t max_seqs, int32_t* cu, int32_t* num_out,
                             hipStream_t s);
 
-// Device ragged-grid build (one workgroup).
+// Device ragged-grid build (one workgroup); also zeroes the kTaskQueues
+// counters at task_counter (kCounterStride apart) when it is not null (the
+// work queues of the persistent launch that follows).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                              int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
-                             int64_t grid_cap, hipStream_t s);
+                             int64_t grid_cap, int32_t* task_counter, hipStream_t s);
 
 }  // namespace vlp
