@@ -365,6 +365,19 @@ __device__ __forceinline__ void attn_bwd_dkdv_f32_task(const BwdArgs& a, int tas
     // P and its dV product first, then dP: fewer score tiles live at once.
     f32x16_t s[NS], dp[NS];
     mma_rows_f32<NS, HALF, RB>(qt, qoff, kv, s);  // S = Q K^T
+    // Masking in a pass of its own, skipped as a whole where no key of the
+    // block needs it (see the 16-bit kernel).
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool vis = q < tc.lq;
+          if (CAUSAL) vis = vis && my_key <= q + diag;
+          if (!vis) s[i][r] = kNegInf;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -374,14 +387,7 @@ __device__ __forceinline__ void attn_bwd_dkdv_f32_task(const BwdArgs& a, int tas
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float sv = s[i][r];
-          if (need_mask) {
-            const int q = qb + qr + e;
-            bool vis = q < tc.lq;
-            if (CAUSAL) vis = vis && my_key <= q + diag;
-            if (!vis) sv = kNegInf;
-          }
-          s[i][r] = fast_exp2(__builtin_fmaf(sv, a.scale_log2, -l4[e]));  // P
+          s[i][r] = fast_exp2(__builtin_fmaf(s[i][r], a.scale_log2, -l4[e]));  // P
         }
       }
     mma_cols_f32<D, NS, DT32, RB>(dot, s, dv, n, hh);  // dV^T += dO^T P
