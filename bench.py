@@ -3,15 +3,20 @@
 One step = one pass of the whole path over one synthetic packed batch:
   1. pack_sequences on the host (lengths -> cu_seqlens, flat_index) into a
      pinned buffer, then an asynchronous copy of cu_seqlens to the device;
-  2. the device ragged-grid build (block_offsets, grid_mapping, tile_order);
-  3. the tiled attention forward (one launch of G_cap * heads workgroups).
+  2. the device ragged-grid build (block_offsets, grid_mapping, tile_order,
+     and the cleared work queues of the persistent schedule);
+  3. the tiled attention forward: one launch of G_cap * heads workgroups,
+     the surplus exiting at once (--schedule persistent: the resident number
+     of workgroups, taking the G * heads active tile tasks from per-XCD work
+     queues).
 Q/K/V are resident in HBM before timing starts.  W warm-up steps, then K
 timed steps bracketed by synchronisation; the host work of step i overlaps the
 GPU work of step i-1.
 
 Also measured in the same run:
-  * the attention kernel alone, K launches timed with HIP events on the stream
-    it runs on (roofline "achieved");
+  * the attention kernel alone, timed with HIP events on the stream it runs
+    on (roofline "achieved"): K launches on a cached grid (static grid), or K
+    calls of the entry point minus K grid builds timed alone (persistent);
   * the padded comparator: torch SDPA over [B, H, L_max, D] on the same GPU
     ("DanLing NestedTensor", Appendix C.8: padded attention is masked SDPA over
     the padded envelope), inputs scattered before timing;
@@ -487,8 +492,9 @@ def bench_overcapture(args, wl, dev) -> int:
         rec = {"capacity_ratio": r, "capacity_tokens": cap_rows, "capacity_seqs": cap_seqs,
                "capacity_tiles": vlp.grid_capacity(cap_rows, cap_seqs, bm),
                "active_tiles": int(np.sum((wl.lengths.astype(np.int64) + bm - 1) // bm))}
+        graphs = {}
         for name, nw in (("static", None), ("persistent", 0)):
-            def step():
+            def step(nw=nw):
                 vlp.varlen_attn_fwd(q, k, v, cu, cu, 0, wl.scale, wl.causal, False, out=out, lse=lse, workspace=ws_f,
                                     num_workers=nw)
                 if args.backward:
@@ -496,20 +502,28 @@ def bench_overcapture(args, wl, dev) -> int:
                                         workspace=ws_b, num_workers=nw)
             step()
             torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
+            graphs[name] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[name]):
                 step()
-            for _ in range(max(args.warmup, 1)):
-                graph.replay()
-            torch.cuda.synchronize()
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ev0.record()
-            for _ in range(reps):
-                graph.replay()
-            ev1.record()
-            torch.cuda.synchronize()
-            rec[f"{name}_ms"] = round(ev0.elapsed_time(ev1) / reps, 4)
-            del graph
+        # both warmed up alike, then timed in alternating rounds (clocks
+        # settle over the first launches of a run): the median round counts
+        for _ in range(max(args.warmup, 1)):
+            for name in graphs:
+                graphs[name].replay()
+        torch.cuda.synchronize()
+        rounds = {name: [] for name in graphs}
+        for rnd in range(5):
+            for name in (("static", "persistent") if rnd % 2 == 0 else ("persistent", "static")):
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for _ in range(reps):
+                    graphs[name].replay()
+                ev1.record()
+                torch.cuda.synchronize()
+                rounds[name].append(ev0.elapsed_time(ev1) / reps)
+        for name, vals in rounds.items():
+            rec[f"{name}_ms"] = round(sorted(vals)[len(vals) // 2], 4)
+        del graphs
         log(f"[bench] overcapture x{r:g}: static {rec['static_ms']:.4f} ms, persistent {rec['persistent_ms']:.4f} ms")
         rows.append(rec)
         del q, k, v, out, lse, ws_f
@@ -517,7 +531,7 @@ def bench_overcapture(args, wl, dev) -> int:
             del dout, grads, ws_b
         torch.cuda.empty_cache()
     print(json.dumps({"mode": "overcapture", "workload": wl.name, "dtype": wl.dtype,
-                      "pass": "forward+backward" if args.backward else "forward", "replays": reps,
+                      "pass": "forward+backward" if args.backward else "forward", "replays": reps, "rounds": 5,
                       "num_seqs": b, "total_tokens": t, "heads": h, "head_dim": d, "causal": wl.causal,
                       "block_m": bm, "rows": rows}), flush=True)
     return 0
@@ -654,6 +668,8 @@ def main() -> int:
                     help="measure the gradients (dq, dk, dv) instead of the forward")
     ap.add_argument("--matmul", choices=["shared", "per-seq"], default=None,
                     help="measure the ragged matrix multiplication on the workload's token split instead")
+    ap.add_argument("--schedule", choices=["static", "persistent"], default="static",
+                    help="forward launch schedule: the static grid (G_cap * heads workgroups) or persistent workers")
     ap.add_argument("--overcapture", default=None, metavar="R1,R2,...",
                     help="graph replays captured for R times the workload's token and sequence capacity, "
                          "static grid against persistent schedule (with --backward: forward and gradients)")
@@ -706,6 +722,8 @@ def main() -> int:
         # one query per sequence: the row cu_seqlens[i] of the packed batch
         q = q[torch.from_numpy(wl.cu_seqlens_host()[:-1]).long().to(dev)].contiguous()
     rows_q = q.shape[0]
+    schedule = args.schedule
+    workers = 0 if schedule == "persistent" else None
     flops = workload_flops(wl, h, first_token=ft)
     out = torch.empty_like(q)
     lse = torch.empty(h, rows_q, dtype=torch.float32, device=dev)
@@ -729,9 +747,9 @@ def main() -> int:
             pinned_q[i].copy_(cuq)
             cu_q_dev.copy_(pinned_q[i], non_blocking=True)
         vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
-                            workspace=ws)
+                            workspace=ws, num_workers=workers)
 
-    log(f"[bench] warmup {args.warmup} steps")
+    log(f"[bench] warmup {args.warmup} steps ({schedule} schedule)")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -748,7 +766,10 @@ def main() -> int:
         vlp.pack_sequences(lengths_host, wl.max_len)
     pack_us = (time.perf_counter() - tp) * 1e6 / 20
 
-    # attention kernel alone: cached device grid, HIP events on the launch stream
+    # Attention kernel alone, HIP events on the launch stream.  Static grid:
+    # launches on a cached device grid.  Persistent schedule (its queues are
+    # cleared by the grid build of each call): calls through the device-grid
+    # entry point minus the same number of grid builds timed alone.
     cu_host = torch.from_numpy(wl.cu_seqlens_host())
     grid_host = vlp.build_ragged_grid(cu_host if ft else torch.from_numpy(wl.cu_seqlens_q_host()), bm)
     grid = vlp.RaggedGrid(grid_host.grid_mapping.to(dev), grid_host.block_offsets.to(dev),
@@ -756,18 +777,34 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
     reps = args.kernel_only_reps or args.steps
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
+
+    def timed(fn) -> float:
         for _ in range(3):
-            vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
-                                grid=grid)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for _ in range(reps):
-            vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal, ft, out=out, lse=lse,
-                                grid=grid)
-        ev1.record(stream)
-    stream.synchronize()
-    kernel_ms = ev0.elapsed_time(ev1) / reps
+            fn()
+        e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    grid_build_ms = None
+    with torch.cuda.stream(stream):
+        if schedule == "persistent":
+            lib = vlp._lib.load()
+            cap = vlp.grid_capacity(b if ft else rows_q, b, bm)
+            g_bo, g_gm, g_to = (torch.empty(n, dtype=torch.int32, device=dev) for n in (b + 1, cap, cap))
+            grid_cu = cu_dev if ft else cu_q_dev
+            call_ms = timed(lambda: vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal,
+                                                        ft, out=out, lse=lse, workspace=ws, num_workers=0))
+            grid_build_ms = timed(lambda: vlp._lib.check(lib.vlp_build_ragged_grid_device(
+                grid_cu.data_ptr(), b, bm, g_bo.data_ptr(), g_gm.data_ptr(), g_to.data_ptr(), cap,
+                stream.cuda_stream), "grid build"))
+            kernel_ms = call_ms - grid_build_ms
+        else:
+            kernel_ms = timed(lambda: vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal,
+                                                          ft, out=out, lse=lse, grid=grid))
     torch.cuda.synchronize()
 
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -831,6 +868,7 @@ def main() -> int:
             "causal": wl.causal,
             "query_is_first_token": ft,
             "block_m": bm,
+            "schedule": schedule,
         },
         "roofline": {**roof, "traffic": traffic},
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
@@ -838,6 +876,8 @@ def main() -> int:
         "padded_ms": None if padded_ms is None else round(padded_ms, 3),
         "padded_backend": padded_backend,
         "kernel_ms": round(kernel_ms, 4),
+        "kernel_timing": ("device-grid calls minus grid builds timed alone (grid build "
+                          f"{grid_build_ms:.4f} ms)" if grid_build_ms is not None else "cached-grid launches"),
         "kernel_tflops": round(achieved, 3),
         "kernel_source_hash": src_hash,
         "algorithmic_gflop": round(flops / 1e9, 3),

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_f32(const BwdArgs a) {
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_bwd_dq_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      attn_bwd_dq_f32_task<D, NW, BN, CAUSAL>(task_args<BwdArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, D >= 64 ? 1 : 2) void attn_bwd_dkdv_f32(co
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_bwd_dkdv_f32_task<D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+      attn_bwd_dkdv_f32_task<D, NW, BQ, CAUSAL>(task_args<BwdArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_h16(const BwdArgs a) {
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_bwd_dq_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      attn_bwd_dq_h16_task<DT, D, NW, BN, CAUSAL>(task_args<BwdArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_h16(c
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_bwd_dkdv_h16_task<DT, D, NW, BQ, CAUSAL>(a, task, lds0, lds1);
+      attn_bwd_dkdv_h16_task<DT, D, NW, BQ, CAUSAL>(task_args<BwdArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_h16(const AttnArgs a) {
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_fwd_h16_task<DT, D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      attn_fwd_h16_task<DT, D, NW, BN, CAUSAL>(task_args<AttnArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_f32(const AttnArgs a) {
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      attn_fwd_f32_task<D, NW, BN, CAUSAL>(a, task, lds0, lds1);
+      attn_fwd_f32_task<D, NW, BN, CAUSAL>(task_args<AttnArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;

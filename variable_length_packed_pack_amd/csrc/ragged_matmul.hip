@@ -214,7 +214,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, WGM * WGN == 4 ? 2 : 1) void ragged
   if constexpr (PERSISTENT) {
     int* mailbox = reinterpret_cast<int*>(lds0);
     run_claimed_tasks(tasks, a.task_counter, mailbox, [&](int task) __attribute__((always_inline)) {
-      ragged_matmul_task<DT, BIAS, BM, BN, WGM, WGN>(a, task, lds0, lds1);
+      ragged_matmul_task<DT, BIAS, BM, BN, WGM, WGN>(task_args<MatmulArgs>(), task, lds0, lds1);
     });
   } else {
     const int task = blockIdx.x;

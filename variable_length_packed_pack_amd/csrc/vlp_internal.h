@@ -155,6 +155,18 @@ constexpr int kTaskQueues = 8;
 // workgroup claims at once); on separate lines they proceed in parallel.
 constexpr int kCounterStride = 64;
 
+// The kernel's argument struct (its first argument, at the start of the
+// kernel-argument segment), read through a pointer the compiler cannot see
+// through: loads of the arguments stay next to their uses in each task
+// instead of being hoisted out of the task loop into scalar registers held
+// across it (which spilled to VGPR lanes).
+template <typename Args>
+__device__ __forceinline__ const Args& task_args() {
+  auto p = __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const Args*)p;
+}
+
 template <typename Fn>
 __device__ __forceinline__ void run_claimed_tasks(int tasks, int32_t* counters, int* mailbox, Fn&& fn) {
   const int w = static_cast<int>(gridDim.x);
