@@ -9,8 +9,12 @@
 // head): bandwidth-bound, so no matrix cores.  One wavefront per (sequence,
 // head), four heads per workgroup.  A key row of one head is split into
 // 16-byte chunks over LPK lanes; the wave covers KPS = 64/LPK keys per step
-// and U steps per round (U*KPS keys in flight) for memory parallelism.  Each
-// key slot keeps its own online-softmax state; slots merge at the end.
+// and U steps per round for memory parallelism: a wave's rounds form a chain
+// of load latencies, so the longest sequences set the kernel's time, and
+// U*KPS = 64 keys are kept in flight (U between 4 and 16, the register
+// budget of the widest rows).  Each key slot keeps its own online-softmax
+// state; slots merge at the end.  The dot products' cross-lane sums use DPP
+// row permutations (group_sum).
 // Sequences run in tile_order (longest first) through the same ragged-grid
 // metadata as the tiled kernel, with one tile per sequence.
 #include <hip/hip_runtime.h>
@@ -87,6 +91,28 @@ template <> struct Chunk<VLP_FP16> {
   }
 };
 
+// Sum over groups of N consecutive lanes (N a power of two <= 64), the result
+// in every lane of the group: DPP lane permutations within rows of 16 lanes
+// (VALU operations, no round trip through the LDS crossbar) -- quad
+// permutations for the lane xor 1 and xor 2 partners, then the half-row and
+// row mirrors, which pair each lane with the other quad / half-row -- and a
+// cross-lane shuffle beyond 16 lanes.  The additions pair the same lanes as
+// an xor butterfly, so the sums are the butterfly's to the bit.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+#pragma unroll
+  for (int off = 16; off < N; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 // Merge two online-softmax states (m in log2 units).
 template <int N>
 __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N], float mo, float lo,
@@ -108,7 +134,7 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
   constexpr int EPC = C::N;        // elements per 16-byte chunk
   constexpr int LPK = D / EPC;     // lanes per key row
   constexpr int KPS = 64 / LPK;    // keys per step
-  constexpr int U = 4;             // steps per round
+  constexpr int U = KPS >= 16 ? 4 : (KPS <= 4 ? 16 : 64 / KPS);  // steps per round (see the header)
   static_assert(LPK >= 1 && LPK <= 64 && (LPK & (LPK - 1)) == 0, "lanes per key");
 
   const int lane = task_tid() & 63;
@@ -159,8 +185,7 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
       float dot = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
-#pragma unroll
-      for (int off = 1; off < LPK; off <<= 1) dot += __shfl_xor(dot, off);
+      dot = group_sum<LPK>(dot);
       if (j < lk_vis) {
         const float s = dot * a.scale_log2;
         const float mn = fmaxf(m, s);
