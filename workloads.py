@@ -196,6 +196,24 @@ def random_dout(total_tokens: int, heads: int, head_dim: int, dtype: str, seed: 
     return torch.from_numpy(a).to(DTYPES[dtype])
 
 
+def random_rows_device(rows: int, heads: int, head_dim: int, dtype: str, seed: int,
+                       device, std: float = 1.0, chunk_rows: int = 1 << 22) -> torch.Tensor:
+    """A [rows, heads, head_dim] tensor of N(0, std^2) values rounded to
+    ``dtype``, drawn on ``device`` by a seeded torch generator in chunks of
+    ``chunk_rows`` rows (for batches too large to draw on the host; the
+    values depend on the seed, the chunking and the device type only)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(rows, heads, head_dim, dtype=DTYPES[dtype], device=device)
+    for r0 in range(0, rows, chunk_rows):
+        n = min(chunk_rows, rows - r0)
+        a = torch.randn(n, heads, head_dim, generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            a *= std
+        out[r0:r0 + n].copy_(a)
+    return out
+
+
 def make_workload(index: int, with_values: bool = True,
                   dtype_override: str | None = None) -> Workload:
     """Build workload ``index`` (1..5) on the host."""
