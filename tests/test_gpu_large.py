@@ -108,3 +108,36 @@ def test_backward_beyond_4gib(batch):
              f"dv {excess[2]:.3e}")
         assert max(excess) <= 0.0
     del out, lse, dq, dk, dv
+
+
+def test_ragged_matmul_beyond_4gib():
+    """x [2^26, 64] (8 GiB) times one [64, 64] weight per sequence (16,384
+    sequences of 4,096 rows); sampled sequences on both sides of the 4 GiB
+    byte offset and the last one against the oracle, with the matmul tests'
+    per-element bound rel * |y| + 2^-14 * (|x| |W|^T) (rel = 2^-8, bf16)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vlp.load_library()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 24 << 30:
+        pytest.skip(f"needs 24 GiB of free device memory, {free >> 30} GiB free")
+    rows, nseq, kdim = 1 << 26, 1 << 14, 64
+    seq = rows // nseq
+    x = workloads.random_rows_device(rows, 1, kdim, "bf16", 5100, DEV).view(rows, kdim)
+    w = (workloads.random_rows_device(nseq, kdim, kdim, "bf16", 5101, DEV).float() / 8).to(torch.bfloat16)
+    cu = torch.arange(0, rows + 1, seq, dtype=torch.int32)
+    y = vlp.ragged_matmul(x, w, cu.to(DEV))
+    torch.cuda.synchronize()
+    one = np.array([0, seq], dtype=np.int32)
+    assert (nseq // 2) * seq * kdim * 2 == 1 << 32  # the sampled sequences straddle the 4 GiB mark
+    for i in (0, nseq // 2 - 1, nseq // 2, nseq - 1):
+        xs = x[i * seq:(i + 1) * seq].float().cpu()
+        ws = w[i:i + 1].float().cpu()
+        ref = oracle.ragged_matmul(xs, ws, one)
+        mag = oracle.ragged_matmul(xs.abs(), ws.abs(), one)
+        got = y[i * seq:(i + 1) * seq].float().cpu().numpy()
+        excess = np.max(np.abs(got - ref) - (2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * mag))
+        _say(f"[large] ragged matmul, sequence {i} (byte offset {i * seq * kdim * 2:#x}): max excess {excess:.3e}")
+        assert excess <= 0.0
+    del x, w, y
+    torch.cuda.empty_cache()
