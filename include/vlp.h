@@ -30,6 +30,13 @@
  *     in particular) are NOT validated: out-of-contract values give undefined
  *     output.  Every argument the host can see is validated before any HIP
  *     call, and a failed check returns a status without touching the GPU.
+ *   - Debugging aid: with VLP_CHECK=1 in the environment, the attention,
+ *     gradient and ragged-matmul entry points first check the cu_seqlens
+ *     contents on the device (cu[0] == 0, non-decreasing, cu[num_seqs] no
+ *     more than the rows of the buffer; in first-token mode every sequence
+ *     non-empty), wait for that check, and return VLP_ERR_INVALID on a
+ *     violation before any other kernel reads the values.  It allocates and
+ *     synchronises, so it is not for captured graphs or timed runs.
  */
 #ifndef VLP_H_
 #define VLP_H_

@@ -46,6 +46,7 @@ SOURCES = [
     "attn_bwd_f32.hip",
     "ragged_matmul.hip",
     "seq_ids.hip",
+    "cu_check.hip",
 ]
 
 

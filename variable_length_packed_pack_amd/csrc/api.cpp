@@ -1,8 +1,9 @@
 // C ABI of libvlp.so: host-side validation, workspace layout and dispatch.
 //
 // Every argument the host can see is checked before any HIP call; device
-// buffer contents (cu_seqlens) are never read on the host, so the forward
-// path enqueues work without synchronising ("gigl.nn.packed_attention":
+// buffer contents (cu_seqlens) are never read on the host (unless VLP_CHECK=1
+// asks for a synchronous debug check), so the forward path enqueues work
+// without synchronising ("gigl.nn.packed_attention":
 // apart from the token count in pack_sequences, the packed path needs no
 // host syncs; "So you wanna CUDA Graph", "Scheduling without max_seqlen":
 // the launch is sized by G_cap, not by reading the lengths).
@@ -10,6 +11,8 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "tile_config.h"
 #include "vlp_internal.h"
@@ -25,6 +28,21 @@ vlp_status hip_status(hipError_t e) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// VLP_CHECK=1 (any value but "0"): check device cu_seqlens contents before
+// anything reads them (synchronous; a debugging aid).
+bool debug_checks() {
+  const char* v = getenv("VLP_CHECK");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+vlp_status check_cu(const int32_t* cu, int32_t num_seqs, int64_t max_total, bool nonempty, hipStream_t s) {
+  if (!cu || !debug_checks()) return VLP_OK;
+  int32_t flags = 0;
+  const vlp_status st = hip_status(vlp::check_cu_seqlens(cu, num_seqs, max_total, nonempty, s, &flags));
+  if (st != VLP_OK) return st;
+  return flags ? VLP_ERR_INVALID : VLP_OK;
+}
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout of the device-built grid: [block_offsets | grid_mapping |
@@ -243,6 +261,9 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
   int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
+  if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
+  if (st != VLP_OK) return st;
   const int32_t* grid_cu = query_is_first_token ? cu_seqlens_k : cu_seqlens_q;
   st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, ctr, s));
   if (st != VLP_OK) return st;
@@ -307,8 +328,11 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
   a.tile_order = tile_order;
   a.num_blocks = static_cast<int32_t>(num_blocks);
   a.grid_cap = static_cast<int32_t>(num_blocks);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid,
-                 static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
+  if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
+  if (st != VLP_OK) return st;
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid, s);
 }
 
 extern "C" const char* vlp_status_string(vlp_status status) {
@@ -422,6 +446,9 @@ vlp_status bwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
 
   char* base = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
+  if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, false, s);
+  if (st != VLP_OK) return st;
   vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
                                  scale, dq, dk, dv, reinterpret_cast<float*>(base + w.off_lse2), c, do_stride,
                                  dq_stride, dkv_stride);
@@ -523,6 +550,9 @@ extern "C" vlp_status vlp_varlen_attn_bwd_grid(
   if ((run_dq && q_num_blocks * heads > INT32_MAX) || (run_dkdv && k_num_blocks * heads > INT32_MAX))
     return VLP_ERR_OVERFLOW;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
+  if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, false, s);
+  if (st != VLP_OK) return st;
   vlp::BwdArgs a = make_bwd_args(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads,
                                  scale, dq, dk, dv, row_stats, c, do_stride, dq_stride, dkv_stride);
   if (run_dq) {
@@ -581,8 +611,9 @@ vlp_status matmul_device_grid(int32_t dtype, const void* x, const void* weight, 
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
   int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  vlp_status st =
-      hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, VLP_MATMUL_BLOCK_M, bo, gm, to, cap, ctr, s));
+  vlp_status st = check_cu(cu_seqlens, num_seqs, rows, false, s);
+  if (st != VLP_OK) return st;
+  st = hip_status(vlp::launch_grid_build(cu_seqlens, num_seqs, VLP_MATMUL_BLOCK_M, bo, gm, to, cap, ctr, s));
   if (st != VLP_OK) return st;
   vlp::MatmulArgs a{};
   a.task_counter = ctr;

@@ -239,6 +239,13 @@ hipError_t launch_attn_bwd_dkdv_f32(const BwdArgs& a, int head_dim, bool causal,
 hipError_t launch_ragged_matmul(int dtype, const MatmulArgs& a, bool bias, int64_t blocks,
                                 int32_t workers, hipStream_t s);
 
+// VLP_CHECK=1 debug validation: checks cu[0] == 0, non-decreasing steps,
+// cu[num_seqs] <= max_total (and non-empty sequences if asked) on the device
+// and waits; *flags != 0 reports a violation (allocates and synchronises:
+// not for captured graphs).
+hipError_t check_cu_seqlens(const int32_t* cu, int32_t num_seqs, int64_t max_total, bool require_nonempty,
+                            hipStream_t s, int32_t* flags);
+
 // Document ids -> cu_seqlens with a fixed capacity (one workgroup).
 hipError_t launch_ids_to_cu(const int32_t* ids, int32_t num_tokens, int32_t max_seqs, int32_t* cu, int32_t* num_out,
                             hipStream_t s);
