@@ -537,6 +537,67 @@ def bench_overcapture(args, wl, dev) -> int:
     return 0
 
 
+def bench_order_ablation(args, wl, dev) -> int:
+    """Tile-order ablation: the attention kernel alone on cached grids, tiles
+    in longest-first order against the natural (sequence) order, the same
+    kernel either way (a NULL tile_order).  On the skewed batch the long
+    sequence sits last as drawn (the worst case for the natural order) and
+    is also moved first.  Prints one JSON line."""
+    import torch
+
+    import variable_length_packed_pack_amd as vlp
+
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    t, h, d, b = wl.total_tokens, wl.heads, wl.head_dim, wl.num_seqs
+    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, False, b, t, wl.max_len)
+    out = torch.empty_like(q)
+    lse = torch.empty(h, t, dtype=torch.float32, device=dev)
+    arrangements = [("as drawn", wl.lengths)]
+    if int(np.argmax(wl.lengths)) != 0:
+        i = int(np.argmax(wl.lengths))
+        arrangements.append(("longest first", np.concatenate([wl.lengths[i:i + 1], wl.lengths[:i],
+                                                               wl.lengths[i + 1:]])))
+    flops = algorithmic_flops(wl.lengths, h, d, wl.causal)
+    stream = torch.cuda.Stream(device=dev)
+    rows = []
+    for name, lengths in arrangements:
+        cu_host = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+        cu = cu_host.to(dev)
+        gh = vlp.build_ragged_grid(cu_host, bm)
+        grids = {"longest-first": vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev),
+                                                 gh.tile_order.to(dev), gh.num_blocks, bm),
+                 "natural": vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev), None,
+                                           gh.num_blocks, bm)}
+        times = {o: [] for o in grids}
+        with torch.cuda.stream(stream):
+            for o in grids:
+                for _ in range(max(args.warmup, 3)):
+                    vlp.varlen_attn_fwd(q, k, v, cu, cu, wl.max_len, wl.scale, wl.causal, out=out, lse=lse,
+                                        grid=grids[o])
+            for rnd in range(5):
+                for o in (grids if rnd % 2 == 0 else reversed(list(grids))):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(args.steps):
+                        vlp.varlen_attn_fwd(q, k, v, cu, cu, wl.max_len, wl.scale, wl.causal, out=out, lse=lse,
+                                            grid=grids[o])
+                    e1.record(stream)
+                    stream.synchronize()
+                    times[o].append(e0.elapsed_time(e1) / args.steps)
+        rec = {"arrangement": name}
+        for o, vals in times.items():
+            ms = sorted(vals)[len(vals) // 2]
+            rec[f"{o}_ms"] = round(ms, 4)
+            rec[f"{o}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+        log(f"[bench] tile order, {name}: longest-first {rec['longest-first_ms']:.4f} ms, "
+            f"natural {rec['natural_ms']:.4f} ms")
+        rows.append(rec)
+    print(json.dumps({"mode": "tile-order ablation", "workload": wl.name, "dtype": wl.dtype, "heads": h,
+                      "head_dim": d, "causal": wl.causal, "block_m": bm, "launches_per_round": args.steps,
+                      "rounds": 5, "rows": rows}), flush=True)
+    return 0
+
+
 def bench_matmul(args, wl, dev) -> int:
     """Ragged matrix multiplication on the workload's token split: the packed
     QKV projection (hidden = heads x head_dim -> 3 x hidden, one shared
@@ -670,6 +731,8 @@ def main() -> int:
                     help="measure the ragged matrix multiplication on the workload's token split instead")
     ap.add_argument("--schedule", choices=["static", "persistent"], default="static",
                     help="forward launch schedule: the static grid (G_cap * heads workgroups) or persistent workers")
+    ap.add_argument("--order-ablation", action="store_true",
+                    help="kernel time with longest-first against natural tile order (skewed: also long first)")
     ap.add_argument("--overcapture", default=None, metavar="R1,R2,...",
                     help="graph replays captured for R times the workload's token and sequence capacity, "
                          "static grid against persistent schedule (with --backward: forward and gradients)")
@@ -709,6 +772,11 @@ def main() -> int:
         return bench_matmul(args, wl, dev)
     if args.overcapture:
         return bench_overcapture(args, wl, dev)
+    if args.order_ablation:
+        if wl.lengths_q is not None:
+            print("--order-ablation runs on workloads whose query and key lengths agree", file=sys.stderr)
+            return 2
+        return bench_order_ablation(args, wl, dev)
     if args.backward:
         if args.first_token:
             print("--backward has no first-token mode", file=sys.stderr)
