@@ -8,13 +8,13 @@ namespace {
 
 template <int D, bool CAUSAL, bool DKDV>
 hipError_t go(const BwdArgs& a, int64_t blocks, int32_t workers, hipStream_t s) {
-  constexpr int NW = tile_waves(VLP_FP32, D);
+  constexpr int NW = tile_waves(VLP_FP32, D);     // dQ: one tile of the forward's query grid
+  constexpr int NWK = VLP_BWD_BLOCK_K / 32;        // dK/dV: one tile of the key grid
   constexpr int BN = tile_block_n(VLP_FP32, D);  // keys (dQ) or queries (dK/dV) per streamed block
-  static_assert(32 * NW == VLP_BWD_BLOCK_K, "the dK/dV kernel covers one tile of the key grid");
   const bool stat = workers == kStaticGrid;
   if (DKDV)
-    return stat ? bwd_go(attn_bwd_dkdv_f32<D, NW, BN, CAUSAL, false>, NW * 64, a, blocks, workers, s)
-                : bwd_go(attn_bwd_dkdv_f32<D, NW, BN, CAUSAL, true>, NW * 64, a, blocks, workers, s);
+    return stat ? bwd_go(attn_bwd_dkdv_f32<D, NWK, BN, CAUSAL, false>, NWK * 64, a, blocks, workers, s)
+                : bwd_go(attn_bwd_dkdv_f32<D, NWK, BN, CAUSAL, true>, NWK * 64, a, blocks, workers, s);
   return stat ? bwd_go(attn_bwd_dq_f32<D, NW, BN, CAUSAL, false>, NW * 64, a, blocks, workers, s)
               : bwd_go(attn_bwd_dq_f32<D, NW, BN, CAUSAL, true>, NW * 64, a, blocks, workers, s);
 }

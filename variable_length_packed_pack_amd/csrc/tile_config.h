@@ -7,11 +7,12 @@
 namespace vlp {
 
 // Waves per workgroup (32 query rows each) and keys per inner step.  Four
-// waves (128-row tiles) for 16-bit head dims 64 and 128: each K/V block in
-// LDS then serves 128 query rows (the encoder batch, D = 64: 8 % faster than
-// 64-row tiles).
+// waves (128-row tiles) for 16-bit head dims 64 and 128 and for fp32 head
+// dim 64: each K/V block in LDS then serves 128 query rows (D = 64: the
+// encoder batch 8 % and the fp32 graph batch ~6 % faster than with 64-row
+// tiles).  fp32 at D = 128 keeps two: four would not fit its registers.
 constexpr int tile_waves(int dtype, int head_dim) {
-  return dtype == VLP_FP32 ? 2 : (head_dim >= 64 ? 4 : 2);
+  return dtype == VLP_FP32 ? (head_dim == 64 ? 4 : 2) : (head_dim >= 64 ? 4 : 2);
 }
 constexpr int tile_block_n(int dtype, int /*head_dim*/) { return dtype == VLP_FP32 ? 32 : 64; }
 constexpr bool head_dim_built(int head_dim) {
