@@ -725,6 +725,9 @@ def main() -> int:
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
     ap.add_argument("--first-token", action="store_true",
                     help="query_is_first_token mode: one query per sequence (its first token)")
+    ap.add_argument("--no-causal", action="store_true",
+                    help="run the workload without its causal mask (e.g. first-token mode over all keys of the "
+                         "Zipf batch's long sequences)")
     ap.add_argument("--backward", action="store_true",
                     help="measure the gradients (dq, dk, dv) instead of the forward")
     ap.add_argument("--matmul", choices=["shared", "per-seq"], default=None,
@@ -768,6 +771,8 @@ def main() -> int:
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)
+    if args.no_causal:
+        wl.causal = False
     if args.matmul:
         return bench_matmul(args, wl, dev)
     if args.overcapture:
@@ -877,7 +882,8 @@ def main() -> int:
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     elt = q.element_size()
-    nbytes = compulsory_bytes(rows_q, t, h, d, elt)
+    # first-token mode reads the visible keys only: one per sequence when causal
+    nbytes = compulsory_bytes(rows_q, b if (ft and wl.causal) else t, h, d, elt)
     if ft:
         # one query per sequence streams all of K and V: bandwidth-bound
         roof = {"bound": "hbm", "achieved": round(nbytes / (kernel_ms * 1e-3) / 1e9, 3), "peak": HBM_PEAK_GBS,
@@ -926,7 +932,7 @@ def main() -> int:
                 "tiny": "8 sequences, U[1,64] lengths, 2 heads x 16, fp32",
                 "cross": "cross-attention: the zipf key lengths (65,536 keys over 64 sequences), ceil(len/4) "
                          "queries each (16,408), 16 heads x 128, non-causal, bf16",
-            }[wl.name],
+            }[wl.name] + ("; run without the causal mask" if args.no_causal else ""),
             "num_seqs": b,
             "total_tokens": t,
             "total_queries": rows_q,

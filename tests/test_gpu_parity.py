@@ -429,3 +429,26 @@ def test_host_grid_matches_device_grid_bitwise():
                        host.num_blocks, bm)
     out2, lse2 = _gpu_forward(wl, grid=g)
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("fp16", 64), ("fp32", 64), ("fp32", 128), ("bf16", 16)])
+def test_first_token_key_split_for_long_sequences(dtype, head_dim):
+    """Sequences of thousands of keys: first-token launches split each
+    sequence's keys over four wavefronts (max_seqlen >= 1024, or a mean
+    length >= 1024 without the hint); every form against the oracle."""
+    lengths = [5000, 3, 1200, 70, 1, 2048]
+    wl = workloads.custom_workload(lengths, 3, head_dim, dtype, False, seed=44)
+    cu = wl.cu_seqlens_host()
+    q = wl.q[torch.from_numpy(cu[:-1]).long()].contiguous()
+    cud = torch.from_numpy(cu).to(DEV)
+    for causal in (False, True):
+        ref, ref_lse = oracle.varlen_attention(q, wl.k, wl.v, None, cu, wl.scale, causal, query_is_first_token=True)
+        for max_seqlen, nw in ((5000, None), (0, None), (5000, 0), (100, None)):
+            out, lse = vlp.varlen_attn_fwd(q.to(DEV), wl.k.to(DEV), wl.v.to(DEV), None, cud, max_seqlen, wl.scale,
+                                           causal, True, num_workers=nw)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(out.float().cpu().numpy() - ref))
+            lerr = np.max(np.abs(lse.cpu().numpy() - ref_lse))
+            _say(f"[parity] first token, long sequences {dtype} D={head_dim} causal={causal} "
+                 f"max_seqlen={max_seqlen} workers={nw}: out {err:.3e} lse {lerr:.3e}")
+            assert err <= TOL_OUT[dtype] and lerr <= TOL_LSE

@@ -140,10 +140,11 @@ vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32
 }
 
 vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int32_t causal, int32_t first_token,
-                   int64_t slots, int32_t workers, hipStream_t s) {
+                   int64_t slots, int32_t workers, int64_t long_keys, hipStream_t s) {
   if (slots <= 0) return VLP_OK;
   if (first_token)
-    return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0, slots, workers, s));
+    return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0,
+                                                   long_keys >= vlp::kFirstTokenSplitKeys, slots, workers, s));
   const int64_t blocks = slots * a.heads;
   if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
   switch (dtype) {
@@ -151,6 +152,12 @@ vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int3
     case VLP_FP16: return hip_status(vlp::launch_attn_f16(a, head_dim, causal != 0, blocks, workers, s));
     default: return hip_status(vlp::launch_attn_f32(a, head_dim, causal != 0, blocks, workers, s));
   }
+}
+
+// Key count that decides the first-token form: the max_seqlen hint, or
+// the mean sequence length when there is none.
+int64_t long_keys(int32_t max_seqlen, int64_t total_k, int32_t num_seqs) {
+  return max_seqlen > 0 ? max_seqlen : total_k / num_seqs;
 }
 
 // The launch-width argument of the persistent entry points: 0 asks for the
@@ -274,7 +281,8 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   a.block_offsets = bo;
   a.tile_order = to;
   a.grid_cap = static_cast<int32_t>(cap);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, s);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, long_keys(max_seqlen, total_k,
+                                                                                         num_seqs), s);
 }
 
 }  // namespace
@@ -332,7 +340,8 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
   if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
   if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
   if (st != VLP_OK) return st;
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid, s);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid,
+                 long_keys(max_seqlen, total_k, num_seqs), s);
 }
 
 extern "C" const char* vlp_status_string(vlp_status status) {

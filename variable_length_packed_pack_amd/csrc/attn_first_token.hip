@@ -127,9 +127,13 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float (&acc)[N],
   m = mn;
 }
 
-// One task: the wavefront's head of the sequence in tile slot `slot`.
-template <int DT, int D, bool CAUSAL>
-__device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, int head) {
+// Online-softmax state of one wave over keys [kb, ke) of sequence `seq`,
+// head `head` (kb, ke already cut to the visible keys).  On return every
+// lane (grp, c) holds the state merged over the wave's KPS key slots for
+// chunk c of the head's row.
+template <int DT, int D>
+__device__ __forceinline__ void first_token_keys(const AttnArgs& a, int seq, int head, int k_start, int kb, int ke,
+                                                 float& m, float& l, float (&acc)[Chunk<DT>::N]) {
   using C = Chunk<DT>;
   constexpr int EPC = C::N;        // elements per 16-byte chunk
   constexpr int LPK = D / EPC;     // lanes per key row
@@ -138,14 +142,6 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
   static_assert(LPK >= 1 && LPK <= 64 && (LPK & (LPK - 1)) == 0, "lanes per key");
 
   const int lane = task_tid() & 63;
-  const int f = a.tile_order ? a.tile_order[slot] : slot;
-  if (f < 0 || f >= a.grid_cap) return;
-  const int seq = a.grid_mapping[f];
-  if (seq < 0 || seq >= a.num_seqs) return;
-  const int k_start = a.cu_k[seq];
-  const int lk = a.cu_k[seq + 1] - k_start;
-  const int lk_vis = CAUSAL ? min(lk, 1) : lk;
-
   const int grp = lane / LPK;   // key slot within a step
   const int c = lane % LPK;     // chunk of the row
 
@@ -161,18 +157,19 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
   const char* vp = static_cast<const char*>(a.v) + kv_off;
   const size_t row_bytes = static_cast<size_t>(a.kv_stride) * (16 / EPC);
 
-  float m = kNegInf, l = 0.0f, acc[EPC];
+  m = kNegInf;
+  l = 0.0f;
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
 
-  for (int j0 = 0; j0 < lk_vis; j0 += U * KPS) {
+  for (int j0 = kb; j0 < ke; j0 += U * KPS) {
     u32x4_t kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * KPS + grp;
       kr[u] = u32x4_t{0, 0, 0, 0};
       vr[u] = kr[u];
-      if (j < lk_vis) {
+      if (j < ke) {
         kr[u] = *reinterpret_cast<const u32x4_t*>(kp + j * row_bytes);
         vr[u] = *reinterpret_cast<const u32x4_t*>(vp + j * row_bytes);
       }
@@ -186,11 +183,11 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
 #pragma unroll
       for (int e = 0; e < EPC; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
       dot = group_sum<LPK>(dot);
-      if (j < lk_vis) {
-        const float s = dot * a.scale_log2;
-        const float mn = fmaxf(m, s);
+      if (j < ke) {
+        const float sc = dot * a.scale_log2;
+        const float mn = fmaxf(m, sc);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        const float p = __builtin_amdgcn_exp2f(s - mn);
+        const float p = __builtin_amdgcn_exp2f(sc - mn);
         float vf[EPC];
         C::widen(vr[u], vf);
         l = l * alpha + p;
@@ -211,51 +208,124 @@ __device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, in
     for (int e = 0; e < EPC; ++e) acco[e] = __shfl_xor(acc[e], off);
     merge_state<EPC>(m, l, acc, mo, lo, acco);
   }
+}
 
-  if (grp == 0) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    float o[EPC];
+// Normalise a merged state and store the output chunk (lanes of key slot 0)
+// and the log-sum-exp (lane 0).
+template <int DT, int D>
+__device__ __forceinline__ void first_token_store(const AttnArgs& a, int seq, int head, float m, float l,
+                                                  const float (&acc)[Chunk<DT>::N]) {
+  using C = Chunk<DT>;
+  constexpr int EPC = C::N;
+  constexpr int LPK = D / EPC;
+  const int lane = task_tid() & 63;
+  if (lane >= LPK) return;
+  const int c = lane;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float o[EPC];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) o[e] = acc[e] * inv;
-    char* op = static_cast<char*>(a.out) +
-               (static_cast<size_t>(seq) * a.o_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
-    *reinterpret_cast<u32x4_t*>(op) = C::narrow(o);
-    if (c == 0 && a.lse)
-      a.lse[static_cast<size_t>(head) * a.rows_q + seq] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
+  for (int e = 0; e < EPC; ++e) o[e] = acc[e] * inv;
+  char* op = static_cast<char*>(a.out) +
+             (static_cast<size_t>(seq) * a.o_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
+  *reinterpret_cast<u32x4_t*>(op) = C::narrow(o);
+  if (c == 0 && a.lse)
+    a.lse[static_cast<size_t>(head) * a.rows_q + seq] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
+}
+
+// Sequence and visible key count of tile slot `slot` (false: no such slot).
+template <bool CAUSAL>
+__device__ __forceinline__ bool first_token_decode(const AttnArgs& a, int slot, int& seq, int& k_start,
+                                                   int& lk_vis) {
+  const int f = a.tile_order ? a.tile_order[slot] : slot;
+  if (f < 0 || f >= a.grid_cap) return false;
+  seq = a.grid_mapping[f];
+  if (seq < 0 || seq >= a.num_seqs) return false;
+  k_start = a.cu_k[seq];
+  const int lk = a.cu_k[seq + 1] - k_start;
+  lk_vis = CAUSAL ? min(lk, 1) : lk;
+  return true;
+}
+
+// One task of the head-parallel form: the wavefront's head of the sequence
+// in tile slot `slot`, all of its keys.
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void first_token_task(const AttnArgs& a, int slot, int head) {
+  int seq, k_start, lk_vis;
+  if (!first_token_decode<CAUSAL>(a, slot, seq, k_start, lk_vis)) return;
+  float m, l, acc[Chunk<DT>::N];
+  first_token_keys<DT, D>(a, seq, head, k_start, 0, lk_vis, m, l, acc);
+  first_token_store<DT, D>(a, seq, head, m, l, acc);
+}
+
+// One task of the key-split form (long sequences): the four waves of the
+// workgroup take consecutive quarters of one head's keys (multiples of 64
+// keys), park their states in LDS, and wave 0 merges them.  A wave's keys
+// are a chain of load latencies, so quartering a long sequence's keys
+// quarters its time.
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void first_token_split_task(const AttnArgs& a, int slot, int head,
+                                                       float (*states)[64][Chunk<DT>::N + 2]) {
+  constexpr int EPC = Chunk<DT>::N;
+  int seq, k_start, lk_vis;
+  if (!first_token_decode<CAUSAL>(a, slot, seq, k_start, lk_vis)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(task_tid() >> 6);
+  const int lane = task_tid() & 63;
+  const int quarter = ((lk_vis + 3) / 4 + 63) / 64 * 64;
+  const int kb = min(lk_vis, wave * quarter), ke = min(lk_vis, kb + quarter);
+  float m, l, acc[EPC];
+  first_token_keys<DT, D>(a, seq, head, k_start, kb, ke, m, l, acc);
+  states[wave][lane][0] = m;
+  states[wave][lane][1] = l;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) states[wave][lane][2 + e] = acc[e];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      float acco[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acco[e] = states[w][lane][2 + e];
+      merge_state<EPC>(m, l, acc, states[w][lane][0], states[w][lane][1], acco);
+    }
+    first_token_store<DT, D>(a, seq, head, m, l, acc);
   }
 }
 
-// Task t = slot * head_groups + group: wave w of the workgroup takes head
-// 4 * group + w.  One task per workgroup on the static grid; tasks from the
-// work queues on the persistent grid.
-template <int DT, int D, bool CAUSAL, bool PERSISTENT>
+// Head-parallel form (SPLIT false): task t = slot * head_groups + group,
+// wave w of the workgroup takes head 4 * group + w.  Key-split form: task
+// t = slot * heads + head, all four waves on that head.  One task per
+// workgroup on the static grid; tasks from the work queues on the
+// persistent grid.
+template <int DT, int D, bool CAUSAL, bool PERSISTENT, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_first_token_kernel(const AttnArgs a, int head_groups) {
   const int wave = threadIdx.x >> 6;
   int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
   g = min(g, a.grid_cap);
   const int tasks = g > 0 ? g * head_groups : 0;
-  if constexpr (PERSISTENT) {
-    __shared__ int mailbox;
-    run_claimed_tasks(tasks, a.task_counter, &mailbox, [&](int task) __attribute__((always_inline)) {
-      const int slot = task / head_groups;
-      const int head = (task - slot * head_groups) * 4 + wave;
-      if (head < a.heads) first_token_task<DT, D, CAUSAL>(a, slot, head);
-    });
-  } else {
-    const int task = blockIdx.x;
-    if (task < tasks) {
-      const int slot = task / head_groups;
+  auto run = [&](int task) __attribute__((always_inline)) {
+    const int slot = task / head_groups;
+    if constexpr (SPLIT) {
+      __shared__ float states[4][64][Chunk<DT>::N + 2];
+      first_token_split_task<DT, D, CAUSAL>(a, slot, task - slot * head_groups, states);
+    } else {
       const int head = (task - slot * head_groups) * 4 + wave;
       if (head < a.heads) first_token_task<DT, D, CAUSAL>(a, slot, head);
     }
+  };
+  if constexpr (PERSISTENT) {
+    __shared__ int mailbox;
+    run_claimed_tasks(tasks, a.task_counter, &mailbox, run);
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) run(task);
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_dt_d(const AttnArgs& a, int64_t slots, int32_t workers, hipStream_t s) {
-  const int head_groups = (a.heads + 3) / 4;
-  const auto kernel = workers == kStaticGrid ? attn_first_token_kernel<DT, D, CAUSAL, false>
-                                             : attn_first_token_kernel<DT, D, CAUSAL, true>;
+  const int head_groups = SPLIT ? a.heads : (a.heads + 3) / 4;
+  const auto kernel = workers == kStaticGrid ? attn_first_token_kernel<DT, D, CAUSAL, false, SPLIT>
+                                             : attn_first_token_kernel<DT, D, CAUSAL, true, SPLIT>;
   int64_t width = 0;
   const hipError_t e = launch_width(kernel, 256, slots * head_groups, workers, &width);
   if (e != hipSuccess) return e;
@@ -263,31 +333,36 @@ hipError_t launch_dt_d(const AttnArgs& a, int64_t slots, int32_t workers, hipStr
   return hipGetLastError();
 }
 
+template <int DT, int D>
+hipError_t launch_dt_dd(const AttnArgs& a, bool causal, bool split, int64_t slots, int32_t workers, hipStream_t s) {
+  if (split)
+    return causal ? launch_dt_d<DT, D, true, true>(a, slots, workers, s)
+                  : launch_dt_d<DT, D, false, true>(a, slots, workers, s);
+  return causal ? launch_dt_d<DT, D, true, false>(a, slots, workers, s)
+                : launch_dt_d<DT, D, false, false>(a, slots, workers, s);
+}
+
 template <int DT>
-hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, int64_t slots, int32_t workers, hipStream_t s) {
-#define VLP_FT_CASE(D)                                                         \
-  case D:                                                                      \
-    return causal ? launch_dt_d<DT, D, true>(a, slots, workers, s)             \
-                  : launch_dt_d<DT, D, false>(a, slots, workers, s);
+hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, bool split, int64_t slots, int32_t workers,
+                     hipStream_t s) {
   switch (head_dim) {
-    VLP_FT_CASE(16)
-    VLP_FT_CASE(32)
-    VLP_FT_CASE(64)
-    VLP_FT_CASE(128)
+    case 16: return launch_dt_dd<DT, 16>(a, causal, split, slots, workers, s);
+    case 32: return launch_dt_dd<DT, 32>(a, causal, split, slots, workers, s);
+    case 64: return launch_dt_dd<DT, 64>(a, causal, split, slots, workers, s);
+    case 128: return launch_dt_dd<DT, 128>(a, causal, split, slots, workers, s);
     default: return hipErrorInvalidValue;
   }
-#undef VLP_FT_CASE
 }
 
 }  // namespace
 
-hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal,
+hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, bool split,
                                    int64_t slots, int32_t workers, hipStream_t s) {
   if (slots <= 0) return hipSuccess;
   switch (dtype) {
-    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, slots, workers, s);
-    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, slots, workers, s);
-    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, slots, workers, s);
+    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, split, slots, workers, s);
+    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, split, slots, workers, s);
+    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, split, slots, workers, s);
     default: return hipErrorInvalidValue;
   }
 }
