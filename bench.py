@@ -941,7 +941,8 @@ def main() -> int:
             "head_dim": d,
             "causal": wl.causal,
             "query_is_first_token": ft,
-            "block_m": bm,
+            # first-token mode has one query per sequence and no query tiles
+            "block_m": None if ft else bm,
             "schedule": schedule,
         },
         "roofline": {**roof, "traffic": traffic},
