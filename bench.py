@@ -54,7 +54,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit tiled attention kernel (the roofline kernel of the
 # bench line); a committed HBM-traffic profile is used only while they match.
-KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_bf16.hip", "tile_config.h", "vlp_internal.h"]
+KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_fwd_pingpong.h", "attn_bf16.hip", "tile_config.h", "vlp_internal.h"]
 METRIC_BWD = "varlen attn bwd TFLOP/s (2.5x forward real-token flops; % MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit dk/dv kernel (the roofline kernel of the backward line).
 KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_bf16.hip", "attn_fwd_mfma.h",
@@ -340,7 +340,7 @@ def bench_backward(args, wl, dev) -> int:
     cu_dev = cu_host.to(dev)
     out, lse = vlp.varlen_attn_fwd(q, k, v, cu_dev, cu_dev, wl.max_len, wl.scale, wl.causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    bm = vlp.kernel_block_m(q.dtype, d, wl.causal, False, b, t, wl.max_len)
+    bm = vlp.bwd_block_m(q.dtype, d, wl.causal)
     ws = torch.empty(vlp.bwd_workspace_size(b, t, t, h, bm), dtype=torch.uint8, device=dev)
     fwd_flops = algorithmic_flops(wl.lengths, h, d, wl.causal)
     flops = 2.5 * fwd_flops
@@ -487,7 +487,8 @@ def bench_overcapture(args, wl, dev) -> int:
             dout = torch.zeros_like(q)
             dout[:t].copy_(dout_host.to(dev))
             grads = tuple(torch.zeros_like(q) for _ in range(3))
-            ws_b = torch.empty(vlp.bwd_workspace_size(cap_seqs, cap_rows, cap_rows, h, bm), dtype=torch.uint8,
+            ws_b = torch.empty(vlp.bwd_workspace_size(cap_seqs, cap_rows, cap_rows, h,
+                                                      vlp.bwd_block_m(tdt, d, wl.causal)), dtype=torch.uint8,
                                device=dev)
         rec = {"capacity_ratio": r, "capacity_tokens": cap_rows, "capacity_seqs": cap_seqs,
                "capacity_tiles": vlp.grid_capacity(cap_rows, cap_seqs, bm),

@@ -168,6 +168,17 @@ int32_t vlp_kernel_block_m(int32_t dtype, int32_t head_dim, int32_t causal,
                            int64_t rows_q, int32_t max_seqlen);
 
 /*
+ * vlp_bwd_block_m -- the query rows per tile of the backward pass's dq phase
+ * (the block_m of its query grid; see vlp_varlen_attn_bwd_grid), or -1 if
+ * the dtype / head_dim combination is unsupported.  It may differ from the
+ * forward's vlp_kernel_block_m (the forward runs 256-row tiles for 16-bit
+ * inputs at head_dim 128, the dq kernel 128-row tiles).  The tiling is the
+ * same ragged grid ("PyCoRa", "Ragged Flash Attention"; "So you wanna CUDA
+ * Graph", "Scheduling without max_seqlen").
+ */
+int32_t vlp_bwd_block_m(int32_t dtype, int32_t head_dim, int32_t causal);
+
+/*
  * vlp_varlen_attn_workspace_size -- bytes of device workspace that
  * vlp_varlen_attn_fwd(_persistent) needs for the device-built grid
  * (block_offsets, grid_mapping, tile_order for G_cap(rows, num_seqs,
@@ -320,7 +331,7 @@ vlp_status vlp_varlen_attn_fwd_persistent(int32_t dtype, const void* q, const vo
  * statistics plus a device-built grid over the query lengths and one over
  * the key lengths (G_cap(rows_q, num_seqs, block_m) and G_cap(total_k,
  * num_seqs, VLP_BWD_BLOCK_K) tiles, each with its work-queue counters),
- * block_m = vlp_kernel_block_m(dtype, head_dim, causal, 0, ...).
+ * block_m = vlp_bwd_block_m(dtype, head_dim, causal).
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, total_k < 0,
  * heads < 1, block_m < 1 -> VLP_ERR_INVALID; rows beyond int32 ->
  * VLP_ERR_OVERFLOW.
@@ -412,8 +423,8 @@ vlp_status vlp_varlen_attn_bwd_persistent(int32_t dtype, const void* q, const vo
  *                  the ragged grid of cu_seqlens_k built with block_m =
  *                  VLP_BWD_BLOCK_K; k_num_blocks * heads workgroups run the
  *                  dk/dv phase.
- *   block_m        the query grid's; must equal vlp_kernel_block_m(dtype,
- *                  head_dim, causal, 0, ...).
+ *   block_m        the query grid's; must equal vlp_bwd_block_m(dtype,
+ *                  head_dim, causal).
  *   row_stats      device fp32 [2, heads, rows_q], 4-byte aligned: written by
  *                  the dq phase (the log-sum-exp in base-2 units and
  *                  rowsum(dout * out) of every owned query row), read by the

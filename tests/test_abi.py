@@ -35,7 +35,8 @@ def test_header_declares_expected_entry_points():
                  "vlp_varlen_attn_fwd_grid", "vlp_build_ragged_grid_device", "vlp_grid_capacity",
                  "vlp_kernel_block_m", "vlp_varlen_attn_workspace_size", "vlp_status_string",
                  "vlp_varlen_attn_bwd", "vlp_varlen_attn_bwd_workspace_size", "vlp_ragged_matmul",
-                 "vlp_varlen_attn_fwd_persistent", "vlp_varlen_attn_bwd_persistent", "vlp_ragged_matmul_persistent"):
+                 "vlp_varlen_attn_fwd_persistent", "vlp_varlen_attn_bwd_persistent", "vlp_ragged_matmul_persistent",
+                 "vlp_bwd_block_m"):
         assert must in names
 
 
@@ -193,6 +194,18 @@ def test_kernel_block_m_and_workspace():
         assert vlp.kernel_block_m(dt, 48) == -1
         assert vlp.kernel_block_m(dt, 256) == -1
     assert vlp.kernel_block_m(torch.int32, 64) == -1
+    # 16-bit head_dim 128 runs the two-group forward (256-row tiles); the
+    # backward's dq phase keeps 128-row tiles.
+    assert vlp.kernel_block_m(torch.bfloat16, 128, True) == 256
+    assert vlp.kernel_block_m(torch.float16, 128) == 256
+    assert vlp.kernel_block_m(torch.float32, 128) == 64
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        for d in (16, 32, 64, 128):
+            bb = vlp.bwd_block_m(dt, d, True)
+            assert bb >= 32 and bb % 32 == 0
+        assert vlp.bwd_block_m(dt, 48) == -1
+    assert vlp.bwd_block_m(torch.bfloat16, 128) == 128
+    assert vlp.bwd_block_m(torch.int32, 64) == -1
     ws = vlp.workspace_size(64, 65536, 128)
     cap = vlp.grid_capacity(65536, 64, 128)
     assert ws >= 4 * (65 + 2 * cap)
@@ -333,7 +346,7 @@ def test_backward_validation_errors():
 
 def test_grid_backward_validation_errors():
     lib = _lib.load()
-    bm = lib.vlp_kernel_block_m(2, 64, 0, 0, 4, 100, 0)
+    bm = lib.vlp_bwd_block_m(2, 64, 0)
 
     def call(**kw):
         a = dict(qgm=FAKE, qbo=FAKE, qn=3, kgm=FAKE, kbo=FAKE, kn=3, bm=bm, stats=FAKE, phases=3, dq=FAKE)

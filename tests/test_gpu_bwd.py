@@ -122,7 +122,7 @@ def test_bwd_workload_every_row(k, dtype):
 @pytest.mark.parametrize("head_dim", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_every_head_dim(dtype, head_dim, causal):
-    bm = vlp.kernel_block_m(workloads.DTYPES[dtype], head_dim, causal)
+    bm = vlp.bwd_block_m(workloads.DTYPES[dtype], head_dim, causal)
     lengths = [1, bm - 1, bm, bm + 1, 3, 2 * bm + 5, 37, 64, 65]
     wl = workloads.custom_workload(lengths, 3, head_dim, dtype, causal, seed=100 + head_dim + causal)
     dout = workloads.random_dout(wl.total_tokens, 3, head_dim, dtype, seed=200 + head_dim)
@@ -234,7 +234,7 @@ def test_bwd_cached_grids_phases_and_tile_order_bitwise():
         gh = vlp.build_ragged_grid(cu, block)
         return vlp.RaggedGrid(gh.grid_mapping.to(DEV), gh.block_offsets.to(DEV), gh.tile_order.to(DEV),
                               gh.num_blocks, block)
-    gq = dev_grid(vlp.kernel_block_m(q.dtype, d, True))
+    gq = dev_grid(vlp.bwd_block_m(q.dtype, d, True))
     gk = dev_grid(vlp.VLP_BWD_BLOCK_K)
     nq, nk = gq._replace(tile_order=None), gk._replace(tile_order=None)
     for grids, phases in (((gq, gk), (3,)), ((gq, gk), (1, 2)), ((nq, nk), (3,))):

@@ -163,6 +163,12 @@ def kernel_block_m(dtype: torch.dtype, head_dim: int, causal: bool = False, quer
                                               int(num_seqs), int(rows_q), int(max_seqlen)))
 
 
+def bwd_block_m(dtype: torch.dtype, head_dim: int, causal: bool = False) -> int:
+    """Query rows per tile of the backward's dq phase (its query grid's block_m)."""
+    code = _DTYPE_CODES.get(dtype, -1)
+    return int(_lib.load().vlp_bwd_block_m(code, int(head_dim), int(causal)))
+
+
 def workspace_size(num_seqs: int, rows_q: int, block_m: int) -> int:
     n = ctypes.c_size_t(0)
     _lib.check(_lib.load().vlp_varlen_attn_workspace_size(int(num_seqs), int(rows_q), int(block_m),
@@ -272,7 +278,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     ``dout`` has the shape of ``out``.  Rows owned by no sequence are never
     written (fresh outputs are allocated with ``torch.empty``).
     ``grids``: cached device metadata ``(query_grid, key_grid)`` from
-    ``build_ragged_grid`` over cu_seqlens_q with the kernel's block_m and over
+    ``build_ragged_grid`` over cu_seqlens_q with ``bwd_block_m`` and over
     cu_seqlens_k with VLP_BWD_BLOCK_K; then ``row_stats`` (fp32 [2, H, rows_q]) carries the row
     statistics from the dq phase to the dk/dv phase and ``phases`` selects
     VLP_BWD_DQ, VLP_BWD_DKDV or both.  ``num_workers``: as for
@@ -330,7 +336,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         _lib.check(st, "varlen_attn_bwd_grid")
         return dq, dk, dv
     if workspace is None:
-        bm = lib.vlp_kernel_block_m(code, head_dim, int(bool(causal)), 0, b, rows_q, int(max_seqlen))
+        bm = lib.vlp_bwd_block_m(code, head_dim, int(bool(causal)))
         if bm < 1:
             raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_bwd")
         nbytes = bwd_workspace_size(b, rows_q, total_k, heads, bm)

@@ -45,6 +45,7 @@ SIGNATURES = {
                                                       ctypes.c_int64, _vp]),
     "vlp_kernel_block_m": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
+    "vlp_bwd_block_m": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "vlp_varlen_attn_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp]),
     "vlp_varlen_attn_fwd": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,

@@ -220,6 +220,13 @@ extern "C" int32_t vlp_kernel_block_m(int32_t dtype, int32_t head_dim, int32_t c
   if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return -1;
   if (!vlp::head_dim_built(head_dim)) return -1;
   if (first_token) return VLP_FIRST_TOKEN_BLOCK_M;
+  return vlp::fwd_block_m(dtype, head_dim);
+}
+
+extern "C" int32_t vlp_bwd_block_m(int32_t dtype, int32_t head_dim, int32_t causal) {
+  (void)causal;
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return -1;
+  if (!vlp::head_dim_built(head_dim)) return -1;
   return 32 * vlp::tile_waves(dtype, head_dim);
 }
 
@@ -388,6 +395,8 @@ vlp_status check_backward(int32_t dtype, const void* q, const void* k, const voi
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return VLP_ERR_INVALID;
   if (rows_q * heads > INT32_MAX || total_k * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  c->block_m = vlp_bwd_block_m(dtype, head_dim, causal);  // the query grid of the dQ kernel
+  if (c->block_m < 1) return VLP_ERR_UNSUPPORTED;
   const int32_t elt = element_bytes(dtype);
   st = resolve_stride(sd.dout, heads, head_dim, elt, do_stride);
   if (st == VLP_OK) st = resolve_stride(sd.dq, heads, head_dim, elt, dq_stride);

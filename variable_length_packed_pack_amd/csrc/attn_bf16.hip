@@ -1,6 +1,8 @@
 // Tiled packed-attention forward, bf16 inputs: template instances and launcher.
-// The kernel itself is described in attn_fwd_mfma.h.
+// The kernels are described in attn_fwd_mfma.h and (head dim 128)
+// attn_fwd_pingpong.h.
 #include "attn_fwd_mfma.h"
+#include "attn_fwd_pingpong.h"
 #include "tile_config.h"
 
 namespace vlp {
@@ -8,15 +10,26 @@ namespace {
 
 template <int D, bool CAUSAL>
 hipError_t go(const AttnArgs& a, int64_t blocks, int32_t workers, hipStream_t s) {
-  constexpr int NW = tile_waves(VLP_BF16, D);
-  constexpr int BN = tile_block_n(VLP_BF16, D);
-  const auto kernel = workers == kStaticGrid ? attn_fwd_h16<VLP_BF16, D, NW, BN, CAUSAL, false>
-                                             : attn_fwd_h16<VLP_BF16, D, NW, BN, CAUSAL, true>;
-  int64_t width = 0;
-  const hipError_t e = launch_width(kernel, NW * 64, blocks, workers, &width);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(NW * 64), 0, s, a);
-  return hipGetLastError();
+  if constexpr (fwd_pingpong(VLP_BF16, D)) {
+    constexpr int BN = tile_block_n(VLP_BF16, D);
+    const auto kernel = workers == kStaticGrid ? attn_fwd_h16_pingpong<VLP_BF16, D, BN, CAUSAL, false>
+                                               : attn_fwd_h16_pingpong<VLP_BF16, D, BN, CAUSAL, true>;
+    int64_t width = 0;
+    const hipError_t e = launch_width(kernel, 512, blocks, workers, &width);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(512), 0, s, a);
+    return hipGetLastError();
+  } else {
+    constexpr int NW = tile_waves(VLP_BF16, D);
+    constexpr int BN = tile_block_n(VLP_BF16, D);
+    const auto kernel = workers == kStaticGrid ? attn_fwd_h16<VLP_BF16, D, NW, BN, CAUSAL, false>
+                                               : attn_fwd_h16<VLP_BF16, D, NW, BN, CAUSAL, true>;
+    int64_t width = 0;
+    const hipError_t e = launch_width(kernel, NW * 64, blocks, workers, &width);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(NW * 64), 0, s, a);
+    return hipGetLastError();
+  }
 }
 
 template <int D>

@@ -15,6 +15,13 @@ constexpr int tile_waves(int dtype, int head_dim) {
   return dtype == VLP_FP32 ? (head_dim == 64 ? 4 : 2) : (head_dim >= 64 ? 4 : 2);
 }
 constexpr int tile_block_n(int dtype, int /*head_dim*/) { return dtype == VLP_FP32 ? 32 : 64; }
+// 16-bit inputs at head dim 128 run the two-group forward (eight waves,
+// 256-row tiles; attn_fwd_pingpong.h); the backward keeps tile_waves.
+constexpr bool fwd_pingpong(int dtype, int head_dim) { return dtype != VLP_FP32 && head_dim == 128; }
+// Query rows per tile of the forward kernels.
+constexpr int fwd_block_m(int dtype, int head_dim) {
+  return fwd_pingpong(dtype, head_dim) ? 256 : 32 * tile_waves(dtype, head_dim);
+}
 constexpr bool head_dim_built(int head_dim) {
   return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
 }
