@@ -82,7 +82,7 @@ def _check_full(wl, causal=None, first_token=False):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("block_m", [32, 64, 128, vlp.VLP_FIRST_TOKEN_BLOCK_M])
+@pytest.mark.parametrize("block_m", [32, 64, 128, 256, vlp.VLP_FIRST_TOKEN_BLOCK_M])
 def test_device_grid_bit_exact(k, block_m):
     lengths = workloads.draw_lengths(k)
     cu = _cu(lengths)
