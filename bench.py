@@ -55,6 +55,10 @@ METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 
 # Sources of the 16-bit tiled attention kernel (the roofline kernel of the
 # bench line); a committed HBM-traffic profile is used only while they match.
 KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_fwd_pingpong.h", "attn_bf16.hip", "tile_config.h", "vlp_internal.h"]
+# ... of the fp32 tiled kernel and of the first-token kernel (their own
+# committed traffic profiles, attn_fwd_<workload> and attn_first_token_<workload>).
+KERNEL_SOURCES_F32 = ["attn_fwd_mfma.h", "attn_f32.hip", "tile_config.h", "vlp_internal.h"]
+KERNEL_SOURCES_FT = ["attn_first_token.hip", "vlp_internal.h"]
 METRIC_BWD = "varlen attn bwd TFLOP/s (2.5x forward real-token flops; % MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit dk/dv kernel (the roofline kernel of the backward line).
 KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_bf16.hip", "attn_fwd_mfma.h",
@@ -894,8 +898,12 @@ def main() -> int:
                 "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    src_hash = kernel_source_hash()
-    traffic = None if ft else traffic_from_profile(args.workload, src_hash)
+    if ft:
+        src_hash = kernel_source_hash(KERNEL_SOURCES_FT)
+        traffic = traffic_from_profile(args.workload, src_hash, kernel="attn_first_token")
+    else:
+        src_hash = kernel_source_hash(KERNEL_SOURCES_F32 if wl.dtype == "fp32" else KERNEL_SOURCES)
+        traffic = traffic_from_profile(args.workload, src_hash)
     log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
 
     padded_ms, padded_backend = (None, "skipped")

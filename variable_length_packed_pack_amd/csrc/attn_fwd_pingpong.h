@@ -168,6 +168,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
     }
   };
 
+  // S^T = K Q^T for the key block in tile kt (MFMA phase).
   auto qk = [&](const char* kt) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -190,6 +191,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
     }
   };
 
+  // O^T += V^T P^T with the packed P of the previous block (MFMA phase).
   auto pv = [&](const char* vt) {
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -217,6 +219,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
     }
   };
 
+  // Mask, online softmax and packing of P for block j (VALU phase).
   auto softmax = [&](int j) {
     const int kb = j * BN;
     const bool need_mask = (kb + BN > tc.lk) || (CAUSAL && kb + BN - 1 > wrow0 + diag);
