@@ -234,6 +234,65 @@ def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
     return total_ms, backend_used
 
 
+def envelope_own_comparator(wl, dev, reps: int, first_token: bool = False):
+    """This library's own forward over the padded envelope: every sequence
+    padded to L_max (queries to the longest query length), cu_seqlens =
+    [0, L, 2L, ...], timing only (random values).  The padded run then costs
+    the same kernel the same work as a rectangular B x L_max grid, which
+    isolates the win of ragged scheduling from the quality of the SDPA
+    backend.  Sequences are taken in equal chunks of at most ~40 GB of
+    q/k/v/out; every chunk does the same work, so the time of one chunk is
+    scaled by B / chunk.  Returns ms (or None if one padded sequence alone
+    exceeds the budget)."""
+    import torch
+    import variable_length_packed_pack_amd as vlp
+
+    b, h, d = wl.num_seqs, wl.heads, wl.head_dim
+    lk = int(wl.max_len)
+    lq = 1 if first_token else int(wl.query_lengths().max())
+    tdt = workloads_dtype(wl.dtype)
+    elt = torch.tensor([], dtype=tdt).element_size()
+    per_seq = (2 * lq + 2 * lk) * h * d * elt
+    chunk = min(b, int(40e9 // per_seq))
+    if chunk < 1:
+        return None
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    q = torch.randn(chunk * lq, h, d, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    k = torch.randn(chunk * lk, h, d, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    v = torch.randn(chunk * lk, h, d, generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    cu_k = (torch.arange(chunk + 1, dtype=torch.int32) * lk).to(dev)
+    cu_q = None if first_token else (torch.arange(chunk + 1, dtype=torch.int32) * lq).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(h, q.shape[0], dtype=torch.float32, device=dev)
+    # the grid runs over the query lengths (first-token mode: over the keys, one tile per sequence)
+    grid_cu = torch.arange(chunk + 1, dtype=torch.int32) * (lk if first_token else lq)
+    bm = vlp.kernel_block_m(tdt, d, wl.causal, first_token, chunk, q.shape[0], lk)
+    gh = vlp.build_ragged_grid(grid_cu, bm)
+    grid = vlp.RaggedGrid(gh.grid_mapping.to(dev), gh.block_offsets.to(dev), gh.tile_order.to(dev), gh.num_blocks, bm)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        def call():
+            vlp.varlen_attn_fwd(q, k, v, cu_q, cu_k, lk, wl.scale, wl.causal, first_token, out=out, lse=lse, grid=grid)
+        call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        stream.synchronize()
+    ms = e0.elapsed_time(e1) / reps * b / chunk
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return ms
+
+
+def workloads_dtype(name: str):
+    import workloads
+    return workloads.DTYPES[name]
+
+
 def cpu_oracle_baseline_bwd(wl, dout, budget_s: float):
     """The oracle's gradients on whole heads of the same batch until the
     budget is spent (at least one head); rate in 2.5x forward flops."""
@@ -907,9 +966,12 @@ def main() -> int:
     log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
 
     padded_ms, padded_backend = (None, "skipped")
+    envelope_ms = None
     if not args.no_padded:
         log("[bench] padded SDPA comparator")
         padded_ms, padded_backend = padded_comparator(wl, q, k, v, reps=3, first_token=ft)
+        log("[bench] own kernel over the padded envelope")
+        envelope_ms = envelope_own_comparator(wl, dev, reps=3, first_token=ft)
     torch.cuda.synchronize()
 
     cpu = None
@@ -959,6 +1021,8 @@ def main() -> int:
         "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
         "padded_ms": None if padded_ms is None else round(padded_ms, 3),
         "padded_backend": padded_backend,
+        "envelope_own_ms": None if envelope_ms is None else round(envelope_ms, 3),
+        "speedup_vs_envelope_own": None if envelope_ms is None else round(envelope_ms / kernel_ms, 3),
         "kernel_ms": round(kernel_ms, 4),
         "kernel_timing": ("device-grid calls minus grid builds timed alone (grid build "
                           f"{grid_build_ms:.4f} ms)" if grid_build_ms is not None else "cached-grid launches"),
