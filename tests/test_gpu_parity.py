@@ -357,6 +357,38 @@ def test_causal_with_longer_keys():
             assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= TOL_LSE
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_cross_lengths_causal_every_kernel(dtype, head_dim):
+    """Lq != Lk in both directions, causal and not, at head dims that run the
+    four-wave kernel (64) and, for 16-bit inputs, the two-group kernel (128):
+    whole 256-row tiles and single waves with no visible key (their rows give
+    0 and lse -inf), tiles whose key range ends inside a block, and key block
+    counts of every residue modulo the three-slot ring."""
+    lq = [600, 5, 300, 1, 257, 130]
+    lk = [100, 9, 700, 1, 3, 200]
+    h = 2
+    rng = np.random.default_rng(100 + head_dim)
+    tdt = workloads.DTYPES[dtype]
+    q = torch.from_numpy(rng.standard_normal((sum(lq), h, head_dim), dtype=np.float32)).to(tdt)
+    k = torch.from_numpy(rng.standard_normal((sum(lk), h, head_dim), dtype=np.float32)).to(tdt)
+    v = torch.from_numpy(rng.standard_normal((sum(lk), h, head_dim), dtype=np.float32)).to(tdt)
+    cq, ck = _cu(lq), _cu(lk)
+    scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+    for causal in (False, True):
+        _say(f"[parity] cross lengths {dtype} D={head_dim} causal={causal}")
+        out, lse = vlp.varlen_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), cq.to(DEV), ck.to(DEV), 0, scale, causal)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.varlen_attention(q, k, v, cq.numpy(), ck.numpy(), scale, causal)
+        got_lse = lse.cpu().numpy()
+        keyless = np.isneginf(ref_lse)
+        assert np.array_equal(np.isneginf(got_lse), keyless)
+        if causal:
+            assert keyless.any()  # the case is exercised
+        assert np.max(np.abs(got_lse[~keyless] - ref_lse[~keyless])) <= TOL_LSE
+        assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= TOL_OUT[dtype]
+
+
 def test_causal_query_sees_no_key_gives_zero_and_neg_inf():
     """Lq > Lk with causal alignment leaves the first Lq - Lk queries keyless."""
     h, d = 1, 64
