@@ -218,12 +218,12 @@ hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t
                            int32_t workers, hipStream_t s);
 
 // First-token forward over `slots` sequences: one wavefront per (sequence,
-// head), or with `split` four wavefronts per (sequence, head), each on a
-// quarter of the keys (long sequences; see kFirstTokenSplitKeys).
+// head), or with `split` eight wavefronts per (sequence, head), each on an
+// eighth of the keys (long sequences; see kFirstTokenSplitKeys).
 hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, bool split,
                                    int64_t slots, int32_t workers, hipStream_t s);
 
-// First-token launches split each sequence's keys over four wavefronts when
+// First-token launches split each sequence's keys over eight wavefronts when
 // the longest sequence (max_seqlen, or the mean length when no hint is
 // given) has at least this many keys.
 constexpr int64_t kFirstTokenSplitKeys = 1024;
