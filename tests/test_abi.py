@@ -450,3 +450,74 @@ def test_sources_never_bit_cast_a_vector_subscript():
     for name in os.listdir(csrc):
         text = open(os.path.join(csrc, name)).read()
         assert not pat.search(text), name
+
+
+def _fwd_tensors(rows=6, heads=2, dim=16, dtype=torch.bfloat16, b=3):
+    q = torch.zeros(rows, heads, dim, dtype=dtype)
+    k = torch.zeros(rows, heads, dim, dtype=dtype)
+    v = torch.zeros(rows, heads, dim, dtype=dtype)
+    cu = torch.tensor([0, 3, 4, 6][: b + 1], dtype=torch.int32)
+    return q, k, v, cu
+
+
+def test_binding_forward_checks_accept_valid_arguments():
+    q, k, v, cu = _fwd_tensors()
+    out = torch.empty_like(q)
+    lse = torch.empty(2, 6, dtype=torch.float32)
+    assert vlp.check_fwd_args(q, k, v, cu, cu, out, lse) == (32, 32, 32)
+    assert vlp.check_fwd_args(q, k, v, cu, cu, None, None)[2] is None
+    qf = torch.zeros(3, 2, 16, dtype=torch.bfloat16)  # first-token mode: one query per sequence
+    assert vlp.check_fwd_args(qf, k, v, None, cu, None, None, query_is_first_token=True)[0] == 32
+
+
+@pytest.mark.parametrize("case", [
+    "cu_q_int64", "cu_k_int64", "cu_q_short", "cu_q_strided", "cu_q_2d", "cu_q_missing", "out_dtype", "out_shape",
+    "out_transposed", "lse_dtype", "lse_shape", "lse_transposed", "kv_dtype", "kv_shape", "first_token_rows",
+])
+def test_binding_forward_checks_reject_bad_arguments(case):
+    """Every tensor argument of varlen_attn_fwd is checked in Python before
+    the library sees a pointer: a wrong cu_seqlens, out or lse would otherwise
+    be read or written out of bounds on the device."""
+    q, k, v, cu = _fwd_tensors()
+    cu_q, cu_k = cu, cu
+    out = torch.empty_like(q)
+    lse = torch.empty(2, 6, dtype=torch.float32)
+    ft = False
+    if case == "cu_q_int64":
+        cu_q = cu.long()
+    elif case == "cu_k_int64":
+        cu_k = cu.long()
+    elif case == "cu_q_short":
+        cu_q = cu[:3].clone()
+    elif case == "cu_q_strided":
+        cu_q = torch.zeros(8, dtype=torch.int32)[::2]
+    elif case == "cu_q_2d":
+        cu_q = cu.view(1, 4)
+    elif case == "cu_q_missing":
+        cu_q = None
+    elif case == "out_dtype":
+        out = torch.empty(q.shape, dtype=torch.float16)
+    elif case == "out_shape":
+        out = torch.empty(5, 2, 16, dtype=q.dtype)
+    elif case == "out_transposed":
+        out = torch.empty(16, 2, 6, dtype=q.dtype).permute(2, 1, 0)
+    elif case == "lse_dtype":
+        lse = torch.empty(2, 6, dtype=torch.float16)
+    elif case == "lse_shape":
+        lse = torch.empty(6, 2, dtype=torch.float32)
+    elif case == "lse_transposed":
+        lse = torch.empty(6, 2, dtype=torch.float32).t()
+    elif case == "kv_dtype":
+        v = v.float()
+    elif case == "kv_shape":
+        v = v[:5]
+    elif case == "first_token_rows":
+        ft = True
+    with pytest.raises((ValueError, TypeError)):
+        vlp.check_fwd_args(q, k, v, cu_q, cu_k, out, lse, query_is_first_token=ft)
+
+
+def test_binding_forward_rejects_host_tensors_before_any_launch():
+    q, k, v, cu = _fwd_tensors()
+    with pytest.raises(ValueError):
+        vlp.varlen_attn_fwd(q, k, v, cu, cu, 4, None, False)

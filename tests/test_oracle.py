@@ -445,6 +445,25 @@ def test_zipf_generator_invariants():
         workloads.zipf_lengths(10, 11, rng)
 
 
+def test_zipf_lengths_match_exact_apportionment():
+    """The Zipf batch's lengths equal the exact rational largest-remainder
+    split of tests/golden/zipf_lengths_workload4.json (written by
+    tests/golden/make_zipf_lengths.py with fractions, not floats)."""
+    doc = json.load(open(os.path.join(GOLDEN, "zipf_lengths_workload4.json")))
+    assert workloads.draw_lengths(4).tolist() == doc["lengths"]
+    assert workloads.draw_lengths(6).tolist() == doc["lengths"]
+    # sequence i's length follows its rank: longer for a smaller rank
+    order = np.argsort(doc["ranks"])
+    assert all(np.diff(np.asarray(doc["lengths"])[order]) <= 0)
+
+
+def test_largest_remainder_apportionment():
+    q = np.asarray([2.5, 1.25, 0.25])
+    assert workloads._largest_remainder(q, 4).tolist() == [3, 1, 0]
+    # equal remainders are served in index order
+    assert workloads._largest_remainder(np.asarray([0.5, 0.5, 1.0]), 2).tolist() == [1, 0, 1]
+
+
 def test_workload_shapes():
     for k in (1, 2, 3, 5):
         lengths = workloads.draw_lengths(k)

@@ -180,6 +180,61 @@ def workspace_size(num_seqs: int, rows_q: int, block_m: int) -> int:
 # attention forward
 # ---------------------------------------------------------------------------
 
+def _check_cu(cu: torch.Tensor, name: str, device: torch.device) -> None:
+    if cu.device != device:
+        raise ValueError(f"{name} must be on {device} (it is on {cu.device})")
+    if cu.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    if cu.dim() != 1 or cu.numel() < 2 or not cu.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 vector [num_seqs + 1]")
+
+
+def check_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: Optional[torch.Tensor],
+                   cu_seqlens_k: torch.Tensor, out: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                   query_is_first_token: bool = False):
+    """Validate the tensors of ``varlen_attn_fwd`` before anything is launched
+    (the caller checks that q is a device tensor).  Every tensor must sit on
+    q's device; cu_seqlens are contiguous int32 [num_seqs + 1] (cu_seqlens_q
+    may be None in first-token mode, where it is not read); ``out`` (if
+    given) has q's dtype and shape and token-major head rows; ``lse`` (if
+    given) is float32 [H, rows_q] and contiguous.  Returns the token strides
+    of q, k/v and out.  Raises ValueError or TypeError."""
+    dev = q.device
+    for name, t in (("k", k), ("v", v)):
+        if t.device != dev:
+            raise ValueError(f"{name} must be on {dev} (it is on {t.device})")
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one of float32 / float16 / bfloat16")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q [rows, H, D] and k, v [T, H, D] with matching H, D")
+    _check_cu(cu_seqlens_k, "cu_seqlens_k", dev)
+    if cu_seqlens_q is None:
+        if not query_is_first_token:
+            raise ValueError("cu_seqlens_q is required unless query_is_first_token")
+    else:
+        _check_cu(cu_seqlens_q, "cu_seqlens_q", dev)
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same number of entries")
+    if query_is_first_token and q.shape[0] != cu_seqlens_k.numel() - 1:
+        raise ValueError("first-token mode takes one query row per sequence")
+    q_st, k_st, v_st = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if k_st != v_st and k.shape[0] > 1:
+        raise ValueError("k and v must share one token stride")
+    o_st = None
+    if out is not None:
+        if out.device != dev or out.dtype != q.dtype or out.shape != q.shape:
+            raise ValueError("out must be a tensor of q's dtype and shape on q's device")
+        o_st = _token_stride(out, "out")
+    if lse is not None:
+        if lse.device != dev:
+            raise ValueError(f"lse must be on {dev}")
+        if lse.dtype != torch.float32:
+            raise TypeError("lse must be float32")
+        if tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [H, rows_q] tensor")
+    return q_st, k_st, o_st
+
+
 def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     cu_seqlens_q: Optional[torch.Tensor], cu_seqlens_k: torch.Tensor,
                     max_seqlen: int = 0, scale: Optional[float] = None, causal: bool = False,
@@ -199,28 +254,25 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     work queues.
     """
     lib = _lib.load()
-    if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens_k.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v and cu_seqlens must be device tensors")
-    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one of float32 / float16 / bfloat16")
-    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
-        raise ValueError("q [rows, H, D] and k, v [T, H, D] with matching H, D")
-    q_st, k_st, v_st = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
-    if k_st != v_st and k.shape[0] > 1:
-        raise ValueError("k and v must share one token stride")
+    q_st, k_st, o_st = check_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, query_is_first_token)
     rows_q, heads, head_dim = (int(x) for x in q.shape)
     total_k = int(k.shape[0])
     b = int(cu_seqlens_k.numel()) - 1
-    if cu_seqlens_k.dtype != torch.int32 or (cu_seqlens_q is not None and cu_seqlens_q.dtype != torch.int32):
-        raise TypeError("cu_seqlens must be int32")
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(head_dim)))
     dev = q.device
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    o_st = _token_stride(out, "out")
+        o_st = _token_stride(out, "out")
     if lse is None and return_lse:
         lse = torch.empty(heads, rows_q, dtype=torch.float32, device=dev)
+    for name, t in (("workspace", workspace),) + (() if grid is None else (
+            ("grid.grid_mapping", grid.grid_mapping), ("grid.block_offsets", grid.block_offsets),
+            ("grid.tile_order", grid.tile_order))):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
     code = _DTYPE_CODES[q.dtype]
     ft = int(bool(query_is_first_token))
     cu_q_ptr = None if (ft and cu_seqlens_q is None) else _ptr(cu_seqlens_q)
@@ -285,9 +337,14 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     ``varlen_attn_fwd`` (device-built grids only), per gradient launch.
     """
     lib = _lib.load()
-    tensors = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k)
-    if not all(t.is_cuda for t in tensors):
-        raise ValueError("all inputs must be device tensors")
+    tensors = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k) + tuple(
+        t for t in (dq, dk, dv, workspace, row_stats) if t is not None)
+    if not q.is_cuda or any(t.device != q.device for t in tensors):
+        raise ValueError("all inputs must be device tensors on q's device")
+    _check_cu(cu_seqlens_q, "cu_seqlens_q", q.device)
+    _check_cu(cu_seqlens_k, "cu_seqlens_k", q.device)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same number of entries")
     if q.dtype not in _DTYPE_CODES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
         raise TypeError("q, k, v, out, dout must share one of float32 / float16 / bfloat16")
     if q.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:] or out.shape != q.shape \
@@ -311,6 +368,12 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != ref.dtype or t.shape != ref.shape:
+            raise ValueError(f"{name} must match the dtype and shape of its input")
+    if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+                                  or tuple(row_stats.shape) != (2, heads, rows_q)):
+        raise ValueError("row_stats must be a contiguous float32 [2, H, rows_q] tensor")
     dq_st, dk_st, dv_st = _token_stride(dq, "dq"), _token_stride(dk, "dk"), _token_stride(dv, "dv")
     if dk_st != dv_st and dk.shape[0] > 1:
         raise ValueError("dk and dv must share one token stride")

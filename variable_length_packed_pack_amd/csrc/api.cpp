@@ -154,9 +154,11 @@ vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int3
   }
 }
 
-// Key count that decides the first-token form: the max_seqlen hint, or
-// the mean sequence length when there is none.
-int64_t long_keys(int32_t max_seqlen, int64_t total_k, int32_t num_seqs) {
+// Key count that decides the first-token form: the keys a query sees in the
+// longest sequence -- one when causal (the query sits at position 0), else
+// the max_seqlen hint, or the mean sequence length when there is none.
+int64_t long_keys(int32_t causal, int32_t max_seqlen, int64_t total_k, int32_t num_seqs) {
+  if (causal) return 1;
   return max_seqlen > 0 ? max_seqlen : total_k / num_seqs;
 }
 
@@ -288,8 +290,8 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   a.block_offsets = bo;
   a.tile_order = to;
   a.grid_cap = static_cast<int32_t>(cap);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, long_keys(max_seqlen, total_k,
-                                                                                         num_seqs), s);
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, long_keys(causal, max_seqlen,
+                                                                                         total_k, num_seqs), s);
 }
 
 }  // namespace
@@ -348,7 +350,7 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
   if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
   if (st != VLP_OK) return st;
   return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid,
-                 long_keys(max_seqlen, total_k, num_seqs), s);
+                 long_keys(causal, max_seqlen, total_k, num_seqs), s);
 }
 
 extern "C" const char* vlp_status_string(vlp_status status) {

@@ -117,28 +117,39 @@ class Workload:
         return int(self.query_lengths().astype(np.int64).sum())
 
 
+def _largest_remainder(quotas: np.ndarray, seats: int) -> np.ndarray:
+    """Integer seats summing to ``seats`` that follow real ``quotas`` (which
+    sum to ``seats``): each entry gets the floor of its quota, and the seats
+    the floors leave over go one each to the entries with the largest
+    fractional parts (Hamilton's apportionment).  Equal fractional parts are
+    served in index order."""
+    seats_of = np.floor(quotas).astype(np.int64)
+    left_over = seats - int(seats_of.sum())
+    # primary key: fractional part, largest first; secondary key: index
+    queue = np.lexsort((np.arange(quotas.size), seats_of - quotas))
+    seats_of[queue[:left_over]] += 1
+    return seats_of
+
+
 def zipf_lengths(total_tokens: int, num_seqs: int, rng: np.random.Generator,
                  exponent: float = 1.0) -> np.ndarray:
-    """Zipf-ranked lengths that sum exactly to ``total_tokens``, each >= 1.
+    """Sequence lengths proportional to rank^-exponent (Zipf), each at least
+    one token, summing exactly to ``total_tokens``; sequence i has rank
+    ``1 + rng.permutation(num_seqs)[i]``.
 
-    Follows the token split described in "So you wanna CUDA Graph" (section
-    "Hello World"): a random rank permutation, weights rank^-s, every sequence
-    gets one token plus the floor of its share of the rest, and the leftover
-    tokens go to the largest fractional parts.  Readings: s = 1, and ties in
-    the fractional parts go to the lower index (stable sort).
+    Every sequence keeps one token; the remaining ``total_tokens - num_seqs``
+    are apportioned in proportion to the Zipf weights by the largest-remainder
+    rule.  This is the token split of "So you wanna CUDA Graph" (section
+    "Hello World"), with the exponent 1 of the Zipf batch and equal remainders
+    resolved in index order.
     """
-    if total_tokens < num_seqs:
-        raise ValueError("total_tokens must provide at least one token per sequence")
-    ranks = rng.permutation(num_seqs).astype(np.float64) + 1.0
-    weights = ranks ** (-exponent)
-    share = weights * ((total_tokens - num_seqs) / weights.sum())
-    extra = np.floor(share).astype(np.int64)
-    remainder = total_tokens - num_seqs - int(extra.sum())
-    if remainder:
-        frac = share - extra
-        order = np.argsort(-frac, kind="stable")
-        extra[order[:remainder]] += 1
-    return (extra + 1).astype(np.int32)
+    spare = total_tokens - num_seqs
+    if spare < 0:
+        raise ValueError(f"{total_tokens} tokens cannot give each of {num_seqs} sequences a token")
+    rank = rng.permutation(num_seqs) + 1
+    weight = rank.astype(np.float64) ** (-exponent)
+    quotas = weight * (spare / weight.sum())
+    return (_largest_remainder(quotas, spare) + 1).astype(np.int32)
 
 
 def draw_lengths(index: int) -> np.ndarray:
