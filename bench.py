@@ -501,6 +501,7 @@ def bench_backward(args, wl, dev) -> int:
         "dkdv_kernel_tflops": roof["achieved"],
         "dq_kernel_tflops": round(1.5 * fwd_flops / (kernel_ms["dq"] * 1e-3) / 1e12, 3),
         "kernel_source_hash": src_hash,
+        "library_build": vlp.build_info(),
         "algorithmic_gflop": round(flops / 1e9, 3),
     }
     print(json.dumps(rec), flush=True)
@@ -832,6 +833,7 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_per_launch": nbytes, "launches": 3}), flush=True)
         return 0
     vlp.load_library()
+    lib_hash = vlp.check_library_current()  # refuses a libvlp.so built from other sources
     k_idx = workloads.WORKLOAD_NAMES[args.workload]
     log(f"[bench] generating workload {args.workload}")
     wl = workloads.make_workload(k_idx)
@@ -1028,6 +1030,7 @@ def main() -> int:
                           f"{grid_build_ms:.4f} ms)" if grid_build_ms is not None else "cached-grid launches"),
         "kernel_tflops": round(achieved, 3),
         "kernel_source_hash": src_hash,
+        "library_build": vlp.build_info(),
         "algorithmic_gflop": round(flops / 1e9, 3),
         "compulsory_gb": round(nbytes / 1e9, 4),
         "rho_seq": round(t / (b * lmax), 4),

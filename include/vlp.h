@@ -552,6 +552,15 @@ vlp_status vlp_ragged_matmul_persistent(int32_t dtype, const void* x, const void
 vlp_status vlp_cu_seqlens_from_ids(const int32_t* ids, int64_t num_tokens, int32_t max_seqs, int32_t* cu_seqlens,
                                    int32_t* num_seqs, void* stream);
 
+/* vlp_build_info -- a static string "csrc=<hash> arch=gfx950" naming the
+ * sources this library was built from: <hash> is the first 16 hex digits of
+ * a SHA-256 over the library's source files and this header (the build
+ * computes it; see variable_length_packed_pack_amd/build.py, source_hash).
+ * Callers compare it with the hash of the sources they hold to make sure a
+ * prebuilt library is not stale.  Never fails; the string is owned by the
+ * library. */
+const char* vlp_build_info(void);
+
 /* vlp_status_string -- a static, human-readable name for a status code; for
  * VLP_ERR_HIP, the text of the last HIP error seen on this thread. */
 const char* vlp_status_string(vlp_status status);

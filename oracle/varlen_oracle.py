@@ -260,8 +260,10 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
     """
     cu_q = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
     cu_k = [int(x) for x in np.asarray(cu_seqlens_k).tolist()]
-    outs, lses = [], []
-    for row, h in samples:
+    # Samples of one (sequence, head) share that sequence's keys: they are
+    # evaluated together, each row exactly as in varlen_attention.
+    groups = {}
+    for n, (row, h) in enumerate(samples):
         seq = None
         for i in range(len(cu_q) - 1):
             if cu_q[i] <= row < cu_q[i + 1]:
@@ -269,15 +271,22 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float,
                 break
         if seq is None:
             raise ValueError(f"row {row} belongs to no sequence")
+        groups.setdefault((seq, h), []).append((n, row))
+    dim = v.shape[2]
+    outs = np.zeros((len(samples), dim))
+    lses = np.zeros(len(samples))
+    for (seq, h), members in groups.items():
         lq = cu_q[seq + 1] - cu_q[seq]
         k0, k1 = cu_k[seq], cu_k[seq + 1]
-        qi = _as_f64(q[row:row + 1, h, :])
+        rows = [row for _, row in members]
+        qi = _as_f64(q[rows, h, :])
         ki = _as_f64(k[k0:k1, h, :])
         vi = _as_f64(v[k0:k1, h, :])
-        o, l = _attend_one(qi, ki, vi, float(scale), causal, [row - cu_q[seq]], lq)
-        outs.append(o[0])
-        lses.append(l[0])
-    return np.asarray(outs), np.asarray(lses)
+        o, l = _attend_one(qi, ki, vi, float(scale), causal, [row - cu_q[seq] for row in rows], lq)
+        for j, (n, _) in enumerate(members):
+            outs[n] = o[j]
+            lses[n] = l[j]
+    return outs, lses
 
 
 # ---------------------------------------------------------------------------

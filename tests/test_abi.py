@@ -521,3 +521,13 @@ def test_binding_forward_rejects_host_tensors_before_any_launch():
     q, k, v, cu = _fwd_tensors()
     with pytest.raises(ValueError):
         vlp.varlen_attn_fwd(q, k, v, cu, cu, 4, None, False)
+
+
+def test_loaded_library_matches_sources():
+    """The library reports the hash of the sources it was built from; it must
+    be the hash of the sources in this tree (a stale prebuilt library fails)."""
+    from variable_length_packed_pack_amd.build import source_hash
+
+    info = vlp.build_info()
+    assert info == f"csrc={source_hash()} arch=gfx950", info
+    assert vlp.check_library_current() == source_hash()

@@ -54,6 +54,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     vlp.load_library()
+    vlp.check_library_current()
     yield
     torch.cuda.synchronize()
 

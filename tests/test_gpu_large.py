@@ -41,6 +41,7 @@ def batch():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     vlp.load_library()
+    vlp.check_library_current()
     free, _ = torch.cuda.mem_get_info()
     if free < 96 << 30:
         pytest.skip(f"needs 96 GiB of free device memory, {free >> 30} GiB free")
@@ -118,6 +119,7 @@ def test_ragged_matmul_beyond_4gib():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     vlp.load_library()
+    vlp.check_library_current()
     free, _ = torch.cuda.mem_get_info()
     if free < 24 << 30:
         pytest.skip(f"needs 24 GiB of free device memory, {free >> 30} GiB free")

@@ -77,6 +77,24 @@ def load_library():
     return _lib.load()
 
 
+def build_info() -> str:
+    """The library's own record of its sources: "csrc=<hash> arch=gfx950"."""
+    return _lib.load().vlp_build_info().decode()
+
+
+def check_library_current() -> str:
+    """Raise unless the loaded libvlp.so was built from the sources in this
+    tree (its compiled-in hash equals build.source_hash()); returns the hash."""
+    from .build import source_hash
+
+    want = source_hash()
+    info = build_info()
+    if f"csrc={want}" not in info.split():
+        raise RuntimeError(f"{_lib.LIB_PATH} is stale: it reports '{info}', the sources hash to {want}; "
+                           "rebuild with `python -m variable_length_packed_pack_amd.build`")
+    return want
+
+
 # ---------------------------------------------------------------------------
 # host metadata
 # ---------------------------------------------------------------------------

@@ -9,6 +9,7 @@ recompiles everything.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -50,9 +51,23 @@ SOURCES = [
 ]
 
 
-def _compile(src: str) -> tuple[str, str]:
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over every file under csrc/ and the
+    public header (names and contents, in name order).  The build compiles it
+    into the library (vlp_build_info), so a loaded libvlp.so can be matched
+    against the sources it claims to come from."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join("csrc", n) for n in os.listdir(CSRC) if os.path.isfile(os.path.join(CSRC, n)))
+    for rel in files + [os.path.join("..", "include", "vlp.h")]:
+        with open(os.path.join(PKG_DIR, rel), "rb") as f:
+            data = f.read()
+        h.update(os.path.basename(rel).encode() + b"\0" + len(data).to_bytes(8, "little") + data)
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, digest: str) -> tuple[str, str]:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, f"-DVLP_SOURCE_HASH=\"{digest}\"", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,8 +82,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    digest = source_hash()
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     objs = [r[0] for r in results]
     if verbose:
         for src, (_, err) in zip(SOURCES, results):

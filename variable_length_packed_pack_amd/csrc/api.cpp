@@ -353,6 +353,12 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
                  long_keys(causal, max_seqlen, total_k, num_seqs), s);
 }
 
+#ifndef VLP_SOURCE_HASH
+#define VLP_SOURCE_HASH "unknown"
+#endif
+
+extern "C" const char* vlp_build_info(void) { return "csrc=" VLP_SOURCE_HASH " arch=gfx950"; }
+
 extern "C" const char* vlp_status_string(vlp_status status) {
   switch (status) {
     case VLP_OK: return "VLP_OK";
