@@ -54,14 +54,14 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "varlen attn fwd real-token TFLOP/s (% MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit tiled attention kernel (the roofline kernel of the
 # bench line); a committed HBM-traffic profile is used only while they match.
-KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_fwd_pingpong.h", "attn_bf16.hip", "tile_config.h", "vlp_internal.h"]
+KERNEL_SOURCES = ["attn_fwd_mfma.h", "attn_fwd_pingpong.h", "attn_h16.hip", "tile_config.h", "vlp_internal.h"]
 # ... of the fp32 tiled kernel and of the first-token kernel (their own
 # committed traffic profiles, attn_fwd_<workload> and attn_first_token_<workload>).
 KERNEL_SOURCES_F32 = ["attn_fwd_mfma.h", "attn_f32.hip", "tile_config.h", "vlp_internal.h"]
 KERNEL_SOURCES_FT = ["attn_first_token.hip", "vlp_internal.h"]
 METRIC_BWD = "varlen attn bwd TFLOP/s (2.5x forward real-token flops; % MFMA peak) + speedup vs padded, 1 GPU"
 # Sources of the 16-bit dk/dv kernel (the roofline kernel of the backward line).
-KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_bf16.hip", "attn_fwd_mfma.h",
+KERNEL_SOURCES_BWD = ["attn_bwd_mfma.h", "attn_bwd_launch.h", "attn_bwd_h16.hip", "attn_fwd_mfma.h",
                       "tile_config.h", "vlp_internal.h"]
 
 

@@ -291,6 +291,34 @@ def test_every_head_dim(dtype, head_dim, causal):
 
 
 @pytest.mark.parametrize("dtype", EDGE_DTYPES)
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("profile", ["ramp", "step"])
+def test_scores_that_outgrow_the_running_max(dtype, head_dim, causal, profile):
+    """Keys whose size grows along each sequence, so that later key blocks
+    score far above every earlier one and the online softmax must move its
+    reference max: "ramp" (key gain 1 + 0.1 j at local position j) moves it
+    by about 14 exp2 units, above the rescale threshold, in every 64-key
+    block; "step" (gain 1 for the first 64 keys, 64 after) jumps by more
+    than 128 exp2 units, beyond the fp32 range of exp2, so no probability
+    formed against the old reference can be kept.  q and k are random signs
+    (times 0.5 and the gain), so every score is exact in fp32 and the
+    comparison measures the softmax, not the rounding of large dot
+    products."""
+    lengths = [700, 65, 1, 300, 129]
+    wl = workloads.custom_workload(lengths, 2, head_dim, dtype, causal, seed=head_dim + (profile == "step"))
+    cu = wl.cu_seqlens_host()
+    gain = torch.ones(wl.total_tokens, 1, 1)
+    for i in range(wl.num_seqs):
+        a, b = int(cu[i]), int(cu[i + 1])
+        pos = torch.arange(b - a, dtype=torch.float32)
+        gain[a:b, 0, 0] = 1.0 + 0.1 * pos if profile == "ramp" else torch.where(pos < 64, 1.0, 64.0)
+    wl.k = (torch.sign(wl.k.float()) * gain).to(wl.q.dtype)
+    wl.q = (0.5 * torch.sign(wl.q.float())).to(wl.q.dtype)
+    _check_full(wl)
+
+
+@pytest.mark.parametrize("dtype", EDGE_DTYPES)
 def test_single_long_sequence(dtype):
     wl = workloads.custom_workload([1000], 2, 64, dtype, False, seed=11)
     _check_full(wl)

@@ -39,11 +39,9 @@ SOURCES = [
     "api.cpp",
     "grid_build.hip",
     "attn_first_token.hip",
-    "attn_bf16.hip",
-    "attn_f16.hip",
+    "attn_h16.hip",
     "attn_f32.hip",
-    "attn_bwd_bf16.hip",
-    "attn_bwd_f16.hip",
+    "attn_bwd_h16.hip",
     "attn_bwd_f32.hip",
     "ragged_matmul.hip",
     "seq_ids.hip",
