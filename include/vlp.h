@@ -288,6 +288,39 @@ vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, const void* k,
                                     const int32_t* tile_order, int64_t num_blocks, int32_t block_m,
                                     void* stream);
 
+/* Bytes of the library-owned device scratch of vlp_varlen_attn_fwd_noalloc
+ * (one copy per GPU, held until the process ends). */
+#define VLP_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * vlp_varlen_attn_fwd_noalloc -- vlp_varlen_attn_fwd without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  The tile metadata the device grid build
+ * writes (vlp_varlen_attn_workspace_size bytes for these sizes) goes into a
+ * file-scope device array of VLP_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library instead, whose address on the current device is looked up once
+ * (hipGetSymbolAddress) on the first call there.  Same kernels, same
+ * arguments (minus workspace) and bit-identical results as
+ * vlp_varlen_attn_fwd on the static grid; nothing in the scratch has to
+ * start at zero (every entry the kernels read is rewritten by the grid build
+ * of the same call).  All calls on one GPU share its scratch: calls that may
+ * overlap on one GPU (different streams without ordering between them) race
+ * and must not be made.  VLP_CHECK=1 is not honoured here (the check
+ * allocates and synchronises).
+ * Errors: as vlp_varlen_attn_fwd; metadata larger than
+ * VLP_NOALLOC_SCRATCH_BYTES (about a million tile slots) -> VLP_ERR_CAPACITY,
+ * checked on the host before any HIP call; a failed symbol lookup ->
+ * VLP_ERR_HIP.
+ */
+vlp_status vlp_varlen_attn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                       int32_t heads, int32_t head_dim, int64_t q_row_stride,
+                                       int64_t kv_row_stride, int64_t out_row_stride, int32_t max_seqlen,
+                                       float scale, int32_t causal, int32_t query_is_first_token,
+                                       void* out, float* lse, void* stream);
+
 /*
  * vlp_varlen_attn_fwd_persistent -- vlp_varlen_attn_fwd with the persistent
  * schedule of "So you wanna CUDA Graph" ("Graph overcapture: bound

@@ -52,6 +52,11 @@ SIGNATURES = {
                                              *[ctypes.c_int64] * 3,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                              _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "vlp_varlen_attn_fwd_noalloc": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                     *[ctypes.c_int64] * 3,
+                                                     ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                                     _vp, _vp, _vp]),
     "vlp_varlen_attn_fwd_persistent": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                                         ctypes.c_int32, *[ctypes.c_int64] * 3,

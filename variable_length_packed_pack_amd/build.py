@@ -46,6 +46,7 @@ SOURCES = [
     "ragged_matmul.hip",
     "seq_ids.hip",
     "cu_check.hip",
+    "noalloc.hip",
 ]
 
 

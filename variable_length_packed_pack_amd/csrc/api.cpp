@@ -257,7 +257,7 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
                            int32_t heads, int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
                            int64_t out_row_stride, int32_t max_seqlen, float scale, int32_t causal,
                            int32_t query_is_first_token, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, int32_t workers, void* stream) {
+                           size_t workspace_bytes, int32_t workers, void* stream, bool debug_check = true) {
   Checked c{};
   vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
                                 head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
@@ -277,9 +277,11 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
   int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
-  if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
-  if (st != VLP_OK) return st;
+  if (debug_check) {
+    if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
+    if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
+    if (st != VLP_OK) return st;
+  }
   const int32_t* grid_cu = query_is_first_token ? cu_seqlens_k : cu_seqlens_q;
   st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, ctr, s));
   if (st != VLP_OK) return st;
@@ -306,6 +308,35 @@ extern "C" vlp_status vlp_varlen_attn_fwd(int32_t dtype, const void* q, const vo
   return fwd_device_grid(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads, head_dim,
                          q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
                          query_is_first_token, out, lse, workspace, workspace_bytes, vlp::kStaticGrid, stream);
+}
+
+extern "C" vlp_status vlp_varlen_attn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v,
+                                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                                  int32_t num_seqs, int64_t rows_q, int64_t total_k, int32_t heads,
+                                                  int32_t head_dim, int64_t q_row_stride, int64_t kv_row_stride,
+                                                  int64_t out_row_stride, int32_t max_seqlen, float scale,
+                                                  int32_t causal, int32_t query_is_first_token, void* out,
+                                                  float* lse, void* stream) {
+  // Sizes first, on the host: a request beyond the scratch is refused before
+  // any HIP call.
+  Checked c{};
+  const vlp_status st = check_forward(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads,
+                                      head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale,
+                                      causal, query_is_first_token, out, &c);
+  if (st != VLP_OK) return st;
+  const int64_t cap = vlp_grid_capacity(c.grid_rows, num_seqs, c.block_m);
+  if (cap > INT32_MAX || cap * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  if (grid_workspace(num_seqs, cap).bytes > vlp::kNoallocScratchBytes) return VLP_ERR_CAPACITY;
+  if (cap == 0) return VLP_OK;
+  void* scratch = nullptr;
+  const vlp_status sst = hip_status(vlp::noalloc_scratch(&scratch));
+  if (sst != VLP_OK) return sst;
+  // The static grid rewrites every metadata entry it reads (the grid build
+  // fills all grid_cap slots), so nothing in the scratch needs clearing.
+  return fwd_device_grid(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads, head_dim,
+                         q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
+                         query_is_first_token, out, lse, scratch, vlp::kNoallocScratchBytes, vlp::kStaticGrid,
+                         stream, /*debug_check=*/false);
 }
 
 extern "C" vlp_status vlp_varlen_attn_fwd_persistent(

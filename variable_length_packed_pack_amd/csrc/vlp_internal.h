@@ -257,6 +257,12 @@ hipError_t check_cu_seqlens(const int32_t* cu, int32_t num_seqs, int64_t max_tot
 hipError_t launch_ids_to_cu(const int32_t* ids, int32_t num_tokens, int32_t max_seqs, int32_t* cu, int32_t* num_out,
                             hipStream_t s);
 
+// Scratch of vlp_varlen_attn_fwd_noalloc: a file-scope device array of this
+// many bytes on every GPU the library runs on; noalloc_scratch returns the
+// current device's copy (its address is looked up once per device).
+constexpr size_t kNoallocScratchBytes = VLP_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
+
 // Device ragged-grid build (one workgroup); also zeroes the kTaskQueues
 // counters at task_counter (kCounterStride apart) when it is not null (the
 // work queues of the persistent launch that follows).
