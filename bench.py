@@ -867,7 +867,8 @@ def main() -> int:
     out = torch.empty_like(q)
     lse = torch.empty(h, rows_q, dtype=torch.float32, device=dev)
     bm = vlp.kernel_block_m(q.dtype, d, wl.causal, ft, b, rows_q, wl.max_len)
-    ws = torch.empty(vlp.workspace_size(b, rows_q, bm), dtype=torch.uint8, device=dev)
+    ws = torch.empty(vlp.fwd_workspace_size(q.dtype, b, rows_q, t, h, d, wl.max_len, wl.causal, ft),
+                     dtype=torch.uint8, device=dev)
     cu_dev = torch.empty(b + 1, dtype=torch.int32, device=dev)
     lengths_host = wl.lengths.copy()
     cross = wl.lengths_q is not None and not ft
@@ -929,16 +930,22 @@ def main() -> int:
         return e0.elapsed_time(e1) / reps
 
     grid_build_ms = None
+    # first-token mode over long sequences runs the chunked form, whose grid
+    # (over the keys, VLP_FIRST_TOKEN_CHUNK_KEYS per tile) only the
+    # device-grid entry points build
+    chunked = ft and not wl.causal and wl.max_len >= vlp.VLP_FIRST_TOKEN_CHUNK_MIN
     with torch.cuda.stream(stream):
-        if schedule == "persistent":
+        if schedule == "persistent" or chunked:
             lib = vlp._lib.load()
-            cap = vlp.grid_capacity(b if ft else rows_q, b, bm)
+            gbm = vlp.VLP_FIRST_TOKEN_CHUNK_KEYS if chunked else bm
+            cap = vlp.grid_capacity(t if chunked else (b if ft else rows_q), b, gbm)
             g_bo, g_gm, g_to = (torch.empty(n, dtype=torch.int32, device=dev) for n in (b + 1, cap, cap))
             grid_cu = cu_dev if ft else cu_q_dev
+            nw = 0 if schedule == "persistent" else None
             call_ms = timed(lambda: vlp.varlen_attn_fwd(q, k, v, cu_q_dev, cu_dev, wl.max_len, wl.scale, wl.causal,
-                                                        ft, out=out, lse=lse, workspace=ws, num_workers=0))
+                                                        ft, out=out, lse=lse, workspace=ws, num_workers=nw))
             grid_build_ms = timed(lambda: vlp._lib.check(lib.vlp_build_ragged_grid_device(
-                grid_cu.data_ptr(), b, bm, g_bo.data_ptr(), g_gm.data_ptr(), g_to.data_ptr(), cap,
+                grid_cu.data_ptr(), b, gbm, g_bo.data_ptr(), g_gm.data_ptr(), g_to.data_ptr(), cap,
                 stream.cuda_stream), "grid build"))
             kernel_ms = call_ms - grid_build_ms
         else:

@@ -183,12 +183,40 @@ int32_t vlp_bwd_block_m(int32_t dtype, int32_t head_dim, int32_t causal);
  * vlp_varlen_attn_fwd(_persistent) needs for the device-built grid
  * (block_offsets, grid_mapping, tile_order for G_cap(rows, num_seqs,
  * block_m) tiles, where rows = rows_q, or num_seqs in first-token mode) and
- * the persistent schedule's work-queue counters.
+ * the persistent schedule's work-queue counters.  Enough for every launch
+ * except first-token mode over long sequences (the chunked form, see
+ * vlp_varlen_attn_fwd_workspace_size, which covers every case).
  * Errors: NULL bytes -> VLP_ERR_NULL; num_seqs < 1, rows_q < 0, block_m < 1
  * -> VLP_ERR_INVALID.
  */
 vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int32_t block_m,
                                           size_t* bytes);
+
+/* Keys per tile of the chunked first-token form, and the longest-sequence
+ * key count from which the device-grid entry points take that form. */
+#define VLP_FIRST_TOKEN_CHUNK_KEYS 4096
+#define VLP_FIRST_TOKEN_CHUNK_MIN 8192
+
+/*
+ * vlp_varlen_attn_fwd_workspace_size -- exact bytes of device workspace that
+ * vlp_varlen_attn_fwd(_persistent) needs for these arguments (each means
+ * what it means there).  In first-token mode without the causal mask, when
+ * the longest sequence (max_seqlen, or the mean length when it is 0) has at
+ * least VLP_FIRST_TOKEN_CHUNK_MIN keys, the forward takes its chunked form
+ * ("gigl.nn.packed_attention", packed_attention with query_is_first_token:
+ * one query per sequence, every key of the sequence): the grid is built over
+ * the keys, VLP_FIRST_TOKEN_CHUNK_KEYS per tile, one workgroup per (tile,
+ * head), and the workspace also
+ * holds the partial softmax states of every (tile, head) -- (head_dim + 4)
+ * floats each -- and one arrival counter per (sequence, head).
+ * Errors: NULL bytes -> VLP_ERR_NULL; dtype or head_dim not built ->
+ * VLP_ERR_UNSUPPORTED; num_seqs < 1, heads < 1, negative counts, causal or
+ * query_is_first_token not 0/1 -> VLP_ERR_INVALID; rows beyond int32 or a
+ * grid of more than int32 (tile, head) tasks -> VLP_ERR_OVERFLOW.
+ */
+vlp_status vlp_varlen_attn_fwd_workspace_size(int32_t dtype, int32_t num_seqs, int64_t rows_q, int64_t total_k,
+                                              int32_t heads, int32_t head_dim, int32_t max_seqlen,
+                                              int32_t causal, int32_t query_is_first_token, size_t* bytes);
 
 /*
  * vlp_varlen_attn_fwd -- packed attention forward, out = softmax(scale q k^T) v
@@ -241,8 +269,8 @@ vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t rows_q, int3
  *   lse            device fp32 [heads, rows_q] or NULL: natural-log
  *                  log-sum-exp of the scaled scores; -inf (and a zero output
  *                  row) for a query that sees no key.
- *   workspace      device, >= vlp_varlen_attn_workspace_size bytes, 256-byte
- *                  aligned; overwritten.
+ *   workspace      device, >= vlp_varlen_attn_fwd_workspace_size bytes,
+ *                  256-byte aligned; overwritten.
  * q, k, v and out must be 16-byte aligned.
  * Errors: NULL q/k/v/out/cu_seqlens_k/workspace (or cu_seqlens_q outside
  * first-token mode) -> VLP_ERR_NULL; dtype or head_dim not built ->

@@ -54,6 +54,8 @@ def test_header_constants_match_binding():
     assert f"#define VLP_BWD_DQ {_lib.VLP_BWD_DQ}" in text and f"#define VLP_BWD_DKDV {_lib.VLP_BWD_DKDV}" in text
     assert f"#define VLP_BWD_BLOCK_K {_lib.VLP_BWD_BLOCK_K}" in text
     assert f"#define VLP_MATMUL_BLOCK_M {_lib.VLP_MATMUL_BLOCK_M}" in text
+    assert f"#define VLP_FIRST_TOKEN_CHUNK_KEYS {_lib.VLP_FIRST_TOKEN_CHUNK_KEYS}" in text
+    assert f"#define VLP_FIRST_TOKEN_CHUNK_MIN {_lib.VLP_FIRST_TOKEN_CHUNK_MIN}" in text
     for name in ("VLP_FP32 = 0", "VLP_FP16 = 1", "VLP_BF16 = 2", "VLP_OK = 0", "VLP_ERR_HIP = 6"):
         assert name in text
 
@@ -209,6 +211,51 @@ def test_kernel_block_m_and_workspace():
     ws = vlp.workspace_size(64, 65536, 128)
     cap = vlp.grid_capacity(65536, 64, 128)
     assert ws >= 4 * (65 + 2 * cap)
+
+
+def test_forward_workspace_size_query():
+    """vlp_varlen_attn_fwd_workspace_size: the grid workspace of
+    vlp_varlen_attn_workspace_size for every tiled launch; first-token mode
+    over sequences of 8192+ keys (the chunked form) adds a grid over the keys
+    in 4096-key tiles, one arrival counter per (sequence, head) and one
+    partial state of head_dim + 4 floats per (tile, head)."""
+    lib = _lib.load()
+    for dt, d in ((torch.bfloat16, 128), (torch.float32, 64), (torch.float16, 16)):
+        for causal in (False, True):
+            bm = vlp.kernel_block_m(dt, d, causal)
+            assert vlp.fwd_workspace_size(dt, 64, 65536, 65536, 16, d, 13802, causal) == vlp.workspace_size(
+                64, 65536, bm)
+    # first-token mode: short sequences, or causal (one key), use the one-tile-per-sequence grid
+    short = vlp.fwd_workspace_size(torch.bfloat16, 64, 64, 65536, 16, 128, 8191, False, True)
+    assert short == vlp.workspace_size(64, 64, vlp.kernel_block_m(torch.bfloat16, 128, False, True))
+    assert vlp.fwd_workspace_size(torch.bfloat16, 64, 64, 65536, 16, 128, 13802, True, True) == short
+    # chunked form: every part of the layout fits
+    ws = vlp.fwd_workspace_size(torch.bfloat16, 64, 64, 65536, 16, 128, 13802, False, True)
+    cap = vlp.grid_capacity(65536, 64, 4096)
+    assert ws >= 4 * (65 + 2 * cap) + 4 * 64 * 16 + 4 * cap * 16 * (128 + 4)
+    # without the hint the mean length (1024 here) decides: not chunked
+    assert vlp.fwd_workspace_size(torch.bfloat16, 64, 64, 65536, 16, 128, 0, False, True) == short
+    n = ctypes.c_size_t(0)
+    fws = lib.vlp_varlen_attn_fwd_workspace_size
+    assert fws(2, 4, 10, 10, 1, 64, 0, 0, 0, None) == _lib.VLP_ERR_NULL
+    assert fws(7, 4, 10, 10, 1, 64, 0, 0, 0, ctypes.addressof(n)) == _lib.VLP_ERR_UNSUPPORTED
+    assert fws(2, 4, 10, 10, 1, 48, 0, 0, 0, ctypes.addressof(n)) == _lib.VLP_ERR_UNSUPPORTED
+    assert fws(2, 0, 10, 10, 1, 64, 0, 0, 0, ctypes.addressof(n)) == _lib.VLP_ERR_INVALID
+    assert fws(2, 4, 10, 10, 0, 64, 0, 0, 0, ctypes.addressof(n)) == _lib.VLP_ERR_INVALID
+    assert fws(2, 4, 10, 10, 1, 64, 0, 2, 0, ctypes.addressof(n)) == _lib.VLP_ERR_INVALID
+    assert fws(2, 4, 1 << 31, 10, 1, 64, 0, 0, 0, ctypes.addressof(n)) == _lib.VLP_ERR_OVERFLOW
+
+
+def test_chunked_first_token_refuses_a_grid_only_workspace():
+    """The chunked form needs more than vlp_varlen_attn_workspace_size gives:
+    a workspace sized that way is refused with VLP_ERR_CAPACITY before any
+    HIP call."""
+    lib = _lib.load()
+    bm = vlp.kernel_block_m(torch.bfloat16, 128, False, True)
+    small = vlp.workspace_size(4, 4, bm)
+    st = lib.vlp_varlen_attn_fwd(2, FAKE, FAKE, FAKE, None, FAKE, 4, 4, 40000, 2, 128, 0, 0, 0, 20000, 0.125, 0, 1,
+                                 FAKE, None, FAKE, small, None)
+    assert st == _lib.VLP_ERR_CAPACITY
 
 
 # --------------------------------------------------------------------------

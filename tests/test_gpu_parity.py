@@ -550,10 +550,56 @@ def test_host_grid_matches_device_grid_bitwise():
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("fp16", 128), ("fp32", 64), ("bf16", 32), ("fp16", 16)])
+def test_first_token_chunked_form(dtype, head_dim):
+    """First-token mode over long sequences with a workspace takes the
+    chunked form: 4096-key tiles, one workgroup per (tile, head), the partial
+    states merged by the last workgroup of each (sequence, head).  Sequences
+    on both sides of the tile boundaries (4095, 4096, 4097, 8192, 12289
+    keys), short ones and a single key, in the static and persistent
+    schedules and through the no-allocation entry point, against the oracle;
+    repeated launches agree bit for bit (the merge order is fixed)."""
+    lengths = [4095, 12289, 1, 4096, 70, 4097, 8192, 300, 5]
+    wl = workloads.custom_workload(lengths, 3, head_dim, dtype, False, seed=61 + head_dim)
+    cu = wl.cu_seqlens_host()
+    q = wl.q[torch.from_numpy(cu[:-1]).long()].contiguous()
+    ref, ref_lse = oracle.varlen_attention(q, wl.k, wl.v, None, cu, wl.scale, False, query_is_first_token=True)
+    qd, kd, vd = q.to(DEV), wl.k.to(DEV), wl.v.to(DEV)
+    cud = torch.from_numpy(cu).to(DEV)
+    first = None
+    for nw in (None, 0, 5):
+        for rep in range(2):
+            out, lse = vlp.varlen_attn_fwd(qd, kd, vd, None, cud, 12289, wl.scale, False, True, num_workers=nw)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(out.float().cpu().numpy() - ref))
+            lerr = np.max(np.abs(lse.cpu().numpy() - ref_lse))
+            _say(f"[parity] first token, chunked {dtype} D={head_dim} workers={nw} rep={rep}: "
+                 f"out {err:.3e} lse {lerr:.3e}")
+            assert err <= TOL_OUT[dtype] and lerr <= TOL_LSE
+            if first is None:
+                first = (out.clone(), lse.clone())
+            else:
+                assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
+    import ctypes
+
+    from variable_length_packed_pack_amd import _lib
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((3, len(lengths)), float("nan"), dtype=torch.float32, device=DEV)
+    code = {"fp32": _lib.VLP_FP32, "fp16": _lib.VLP_FP16, "bf16": _lib.VLP_BF16}[dtype]
+    st = _lib.load().vlp_varlen_attn_fwd_noalloc(
+        code, ctypes.c_void_p(qd.data_ptr()), ctypes.c_void_p(kd.data_ptr()), ctypes.c_void_p(vd.data_ptr()), None,
+        ctypes.c_void_p(cud.data_ptr()), len(lengths), len(lengths), kd.shape[0], 3, head_dim, 0, 0, 0, 12289,
+        wl.scale, 0, 1, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == _lib.VLP_OK
+    torch.cuda.synchronize()
+    assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
+
+
 @pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("fp16", 64), ("fp32", 64), ("fp32", 128), ("bf16", 16)])
 def test_first_token_key_split_for_long_sequences(dtype, head_dim):
     """Sequences of thousands of keys: first-token launches split each
-    sequence's keys over four wavefronts (max_seqlen >= 1024, or a mean
+    sequence's keys over eight wavefronts (max_seqlen >= 1024, or a mean
     length >= 1024 without the hint); every form against the oracle."""
     lengths = [5000, 3, 1200, 70, 1, 2048]
     wl = workloads.custom_workload(lengths, 3, head_dim, dtype, False, seed=44)

@@ -40,6 +40,8 @@ from ._lib import (  # noqa: F401
     VLP_BWD_DQ,
     VLP_DEVICE_SORT_MAX_SEQS,
     VLP_FIRST_TOKEN_BLOCK_M,
+    VLP_FIRST_TOKEN_CHUNK_KEYS,
+    VLP_FIRST_TOKEN_CHUNK_MIN,
     VLP_FP16,
     VLP_FP32,
     VLP_MATMUL_BLOCK_M,
@@ -194,6 +196,18 @@ def workspace_size(num_seqs: int, rows_q: int, block_m: int) -> int:
     return int(n.value)
 
 
+def fwd_workspace_size(dtype: torch.dtype, num_seqs: int, rows_q: int, total_k: int, heads: int, head_dim: int,
+                       max_seqlen: int = 0, causal: bool = False, query_is_first_token: bool = False) -> int:
+    """Bytes of workspace varlen_attn_fwd needs for these arguments (every
+    form, including first-token mode over long sequences)."""
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().vlp_varlen_attn_fwd_workspace_size(
+        _DTYPE_CODES.get(dtype, -1), int(num_seqs), int(rows_q), int(total_k), int(heads), int(head_dim),
+        int(max_seqlen), int(bool(causal)), int(bool(query_is_first_token)), ctypes.addressof(n)),
+        "fwd_workspace_size")
+    return int(n.value)
+
+
 # ---------------------------------------------------------------------------
 # attention forward
 # ---------------------------------------------------------------------------
@@ -308,10 +322,7 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _lib.check(st, "varlen_attn_fwd_grid")
         return out, lse
     if workspace is None:
-        bm = lib.vlp_kernel_block_m(code, head_dim, int(bool(causal)), ft, b, rows_q, int(max_seqlen))
-        if bm < 1:
-            raise _lib.VlpError(_lib.VLP_ERR_UNSUPPORTED, "varlen_attn_fwd")
-        nbytes = workspace_size(b, b if ft else rows_q, bm)
+        nbytes = fwd_workspace_size(q.dtype, b, rows_q, total_k, heads, head_dim, max_seqlen, causal, ft)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     args = (code, _ptr(q), _ptr(k), _ptr(v), cu_q_ptr, _ptr(cu_seqlens_k), b, rows_q, total_k, heads, head_dim,
             q_st, k_st, o_st, int(max_seqlen), float(scale), int(bool(causal)), ft, _ptr(out), _ptr(lse),

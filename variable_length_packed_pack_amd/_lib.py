@@ -30,6 +30,8 @@ VLP_BWD_DQ = 1
 VLP_BWD_DKDV = 2
 VLP_BWD_BLOCK_K = 64
 VLP_MATMUL_BLOCK_M = 128
+VLP_FIRST_TOKEN_CHUNK_KEYS = 4096
+VLP_FIRST_TOKEN_CHUNK_MIN = 8192
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -47,6 +49,9 @@ SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "vlp_bwd_block_m": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "vlp_varlen_attn_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp]),
+    "vlp_varlen_attn_fwd_workspace_size": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp]),
     "vlp_varlen_attn_fwd": (ctypes.c_int32, [ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                              *[ctypes.c_int64] * 3,

@@ -140,11 +140,10 @@ vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32
 }
 
 vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int32_t causal, int32_t first_token,
-                   int64_t slots, int32_t workers, int64_t long_keys, hipStream_t s) {
+                   int64_t slots, int32_t workers, vlp::FirstTokenForm form, hipStream_t s) {
   if (slots <= 0) return VLP_OK;
   if (first_token)
-    return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0,
-                                                   long_keys >= vlp::kFirstTokenSplitKeys, slots, workers, s));
+    return hip_status(vlp::launch_attn_first_token(dtype, a, head_dim, causal != 0, form, slots, workers, s));
   const int64_t blocks = slots * a.heads;
   if (blocks > INT32_MAX) return VLP_ERR_OVERFLOW;
   switch (dtype) {
@@ -160,6 +159,44 @@ vlp_status enqueue(int32_t dtype, const vlp::AttnArgs& a, int32_t head_dim, int3
 int64_t long_keys(int32_t causal, int32_t max_seqlen, int64_t total_k, int32_t num_seqs) {
   if (causal) return 1;
   return max_seqlen > 0 ? max_seqlen : total_k / num_seqs;
+}
+
+// Form of a first-token launch; the chunked form needs a workspace (its
+// partial states), so the cached-grid entry point never takes it.
+vlp::FirstTokenForm first_token_form(int32_t causal, int32_t max_seqlen, int64_t total_k, int32_t num_seqs,
+                                     bool with_workspace) {
+  const int64_t keys = long_keys(causal, max_seqlen, total_k, num_seqs);
+  if (with_workspace && keys >= vlp::kFirstTokenChunkMin) return vlp::FirstTokenForm::kChunked;
+  return keys >= vlp::kFirstTokenSplitKeys ? vlp::FirstTokenForm::kKeySplit : vlp::FirstTokenForm::kHeadParallel;
+}
+
+// Workspace of the device-grid forward: the grid (GridWorkspace) and, for
+// the chunked first-token form, per-(sequence, head) arrival counters and
+// the per-(chunk, head) partial states, each 256-byte aligned.
+struct FwdWorkspace {
+  GridWorkspace grid;
+  int32_t block_m;           // rows (keys, chunked form) per tile of the grid
+  int64_t cap;               // grid capacity
+  vlp::FirstTokenForm form;
+  size_t off_arrivals, off_partials, bytes;
+};
+
+vlp_status fwd_workspace(const Checked& c, int32_t num_seqs, int64_t total_k, int32_t heads, int32_t head_dim,
+                         int32_t causal, int32_t first_token, int32_t max_seqlen, FwdWorkspace* w) {
+  w->form = first_token ? first_token_form(causal, max_seqlen, total_k, num_seqs, true)
+                        : vlp::FirstTokenForm::kHeadParallel;
+  const bool chunked = first_token && w->form == vlp::FirstTokenForm::kChunked;
+  w->block_m = chunked ? static_cast<int32_t>(vlp::kFirstTokenChunkKeys) : c.block_m;
+  w->cap = vlp_grid_capacity(chunked ? total_k : c.grid_rows, num_seqs, w->block_m);
+  if (w->cap > INT32_MAX || w->cap * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
+  w->grid = grid_workspace(num_seqs, w->cap);
+  w->off_arrivals = w->off_partials = w->bytes = w->grid.bytes;
+  if (chunked) {
+    w->off_arrivals = round_up(w->grid.bytes, 256);
+    w->off_partials = w->off_arrivals + round_up(sizeof(int32_t) * static_cast<size_t>(num_seqs) * heads, 256);
+    w->bytes = w->off_partials + sizeof(float) * static_cast<size_t>(w->cap) * heads * (head_dim + 4);
+  }
+  return VLP_OK;
 }
 
 // The launch-width argument of the persistent entry points: 0 asks for the
@@ -241,6 +278,28 @@ extern "C" vlp_status vlp_varlen_attn_workspace_size(int32_t num_seqs, int64_t r
   return VLP_OK;
 }
 
+extern "C" vlp_status vlp_varlen_attn_fwd_workspace_size(int32_t dtype, int32_t num_seqs, int64_t rows_q,
+                                                         int64_t total_k, int32_t heads, int32_t head_dim,
+                                                         int32_t max_seqlen, int32_t causal,
+                                                         int32_t query_is_first_token, size_t* bytes) {
+  if (!bytes) return VLP_ERR_NULL;
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
+  if (!vlp::head_dim_built(head_dim)) return VLP_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || heads < 1 || rows_q < 0 || total_k < 0 || max_seqlen < 0) return VLP_ERR_INVALID;
+  if ((causal != 0 && causal != 1) || (query_is_first_token != 0 && query_is_first_token != 1))
+    return VLP_ERR_INVALID;
+  if (rows_q > INT32_MAX || total_k > INT32_MAX) return VLP_ERR_OVERFLOW;
+  Checked c{};
+  c.block_m = vlp_kernel_block_m(dtype, head_dim, causal, query_is_first_token, num_seqs, rows_q, max_seqlen);
+  c.grid_rows = query_is_first_token ? num_seqs : rows_q;
+  FwdWorkspace fw{};
+  const vlp_status st =
+      fwd_workspace(c, num_seqs, total_k, heads, head_dim, causal, query_is_first_token, max_seqlen, &fw);
+  if (st != VLP_OK) return st;
+  *bytes = fw.bytes;
+  return VLP_OK;
+}
+
 extern "C" vlp_status vlp_build_ragged_grid_device(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                                                    int32_t* block_offsets, int32_t* grid_mapping,
                                                    int32_t* tile_order, int64_t grid_cap, void* stream) {
@@ -265,17 +324,21 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   if (st != VLP_OK) return st;
   if (!workspace) return VLP_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return VLP_ERR_INVALID;
-  const int64_t cap = vlp_grid_capacity(c.grid_rows, num_seqs, c.block_m);
-  if (cap > INT32_MAX || cap * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
-  const GridWorkspace w = grid_workspace(num_seqs, cap);
-  if (workspace_bytes < w.bytes) return VLP_ERR_CAPACITY;
+  FwdWorkspace fw{};
+  st = fwd_workspace(c, num_seqs, total_k, heads, head_dim, causal, query_is_first_token, max_seqlen, &fw);
+  if (st != VLP_OK) return st;
+  if (workspace_bytes < fw.bytes) return VLP_ERR_CAPACITY;
+  const int64_t cap = fw.cap;
   if (cap == 0) return VLP_OK;
 
+  const GridWorkspace& w = fw.grid;
   char* base = static_cast<char*>(workspace);
   int32_t* bo = reinterpret_cast<int32_t*>(base + w.off_bo);
   int32_t* gm = reinterpret_cast<int32_t*>(base + w.off_gm);
   int32_t* to = reinterpret_cast<int32_t*>(base + w.off_to);
   int32_t* ctr = workers == vlp::kStaticGrid ? nullptr : reinterpret_cast<int32_t*>(base + w.off_ctr);
+  const bool chunked = query_is_first_token && fw.form == vlp::FirstTokenForm::kChunked;
+  int32_t* arrivals = chunked ? reinterpret_cast<int32_t*>(base + fw.off_arrivals) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_check) {
     if (!query_is_first_token) st = check_cu(cu_seqlens_q, num_seqs, rows_q, false, s);
@@ -283,7 +346,10 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
     if (st != VLP_OK) return st;
   }
   const int32_t* grid_cu = query_is_first_token ? cu_seqlens_k : cu_seqlens_q;
-  st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, c.block_m, bo, gm, to, cap, ctr, s));
+  // The grid build also clears the chunked form's arrival counters, so the
+  // sequence stays free of memsets (capture-safe).
+  st = hip_status(vlp::launch_grid_build(grid_cu, num_seqs, fw.block_m, bo, gm, to, cap, ctr, s, arrivals,
+                                         chunked ? num_seqs * heads : 0));
   if (st != VLP_OK) return st;
 
   vlp::AttnArgs a = make_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, heads, scale, out, lse, c);
@@ -292,8 +358,9 @@ vlp_status fwd_device_grid(int32_t dtype, const void* q, const void* k, const vo
   a.block_offsets = bo;
   a.tile_order = to;
   a.grid_cap = static_cast<int32_t>(cap);
-  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, long_keys(causal, max_seqlen,
-                                                                                         total_k, num_seqs), s);
+  a.ft_arrivals = arrivals;
+  a.ft_partials = chunked ? reinterpret_cast<float*>(base + fw.off_partials) : nullptr;
+  return enqueue(dtype, a, head_dim, causal, query_is_first_token, cap, workers, fw.form, s);
 }
 
 }  // namespace
@@ -324,15 +391,18 @@ extern "C" vlp_status vlp_varlen_attn_fwd_noalloc(int32_t dtype, const void* q, 
                                       head_dim, q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale,
                                       causal, query_is_first_token, out, &c);
   if (st != VLP_OK) return st;
-  const int64_t cap = vlp_grid_capacity(c.grid_rows, num_seqs, c.block_m);
-  if (cap > INT32_MAX || cap * heads > INT32_MAX) return VLP_ERR_OVERFLOW;
-  if (grid_workspace(num_seqs, cap).bytes > vlp::kNoallocScratchBytes) return VLP_ERR_CAPACITY;
-  if (cap == 0) return VLP_OK;
+  FwdWorkspace fw{};
+  const vlp_status wst = fwd_workspace(c, num_seqs, total_k, heads, head_dim, causal, query_is_first_token,
+                                       max_seqlen, &fw);
+  if (wst != VLP_OK) return wst;
+  if (fw.bytes > vlp::kNoallocScratchBytes) return VLP_ERR_CAPACITY;
+  if (fw.cap == 0) return VLP_OK;
   void* scratch = nullptr;
   const vlp_status sst = hip_status(vlp::noalloc_scratch(&scratch));
   if (sst != VLP_OK) return sst;
   // The static grid rewrites every metadata entry it reads (the grid build
-  // fills all grid_cap slots), so nothing in the scratch needs clearing.
+  // fills all grid_cap slots and clears the chunked first-token form's
+  // counters), so nothing in the scratch needs clearing here.
   return fwd_device_grid(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, rows_q, total_k, heads, head_dim,
                          q_row_stride, kv_row_stride, out_row_stride, max_seqlen, scale, causal,
                          query_is_first_token, out, lse, scratch, vlp::kNoallocScratchBytes, vlp::kStaticGrid,
@@ -381,7 +451,7 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
   if (st == VLP_OK) st = check_cu(cu_seqlens_k, num_seqs, total_k, query_is_first_token != 0, s);
   if (st != VLP_OK) return st;
   return enqueue(dtype, a, head_dim, causal, query_is_first_token, num_blocks, vlp::kStaticGrid,
-                 long_keys(causal, max_seqlen, total_k, num_seqs), s);
+                 first_token_form(causal, max_seqlen, total_k, num_seqs, false), s);
 }
 
 #ifndef VLP_SOURCE_HASH

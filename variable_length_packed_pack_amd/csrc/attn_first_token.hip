@@ -293,6 +293,126 @@ __device__ __forceinline__ void first_token_split_task(const AttnArgs& a, int sl
   }
 }
 
+// One task of the chunked form (long sequences, with a workspace): the grid
+// is built over the keys with kFirstTokenChunkKeys keys per tile, and the
+// workgroup's kSplitWaves waves take consecutive shares of its chunk of one
+// head's keys, merged in LDS by wave 0 as in the key-split form.  A sequence
+// of one chunk is stored at once.  Otherwise wave 0 publishes the chunk's
+// state in the workspace (ft_partials), and the workgroup that brings the
+// (sequence, head)'s arrival counter to the chunk count merges every chunk's
+// state in chunk order -- so the result does not depend on which one
+// finishes last -- stores the output and clears the counter.  The
+// device-scope fences order the state stores before the counter update and
+// the counter read before the state loads (the XCDs' L2 caches are not
+// coherent with one another within a launch).
+template <int DT, int D>
+__device__ __forceinline__ void first_token_chunk_task(const AttnArgs& a, int slot, int head,
+                                                       float (*states)[64][Chunk<DT>::N + 2]) {
+  constexpr int EPC = Chunk<DT>::N;
+  constexpr int LPK = D / EPC;
+  constexpr int STRIDE = D + 4;  // floats per published state: m, l, two unused, acc[D]
+  const int f = a.tile_order ? a.tile_order[slot] : slot;
+  if (f < 0 || f >= a.grid_cap) return;
+  const int seq = a.grid_mapping[f];
+  if (seq < 0 || seq >= a.num_seqs) return;
+  const int first = a.block_offsets[seq];
+  const int nchunks = a.block_offsets[seq + 1] - first;
+  const int k_start = a.cu_k[seq];
+  const int lk = a.cu_k[seq + 1] - k_start;
+  const int cb = (f - first) * static_cast<int>(kFirstTokenChunkKeys);
+  const int ce = min(lk, cb + static_cast<int>(kFirstTokenChunkKeys));
+  const int wave = __builtin_amdgcn_readfirstlane(task_tid() >> 6);
+  const int lane = task_tid() & 63;
+  const int share = ((ce - cb + kSplitWaves - 1) / kSplitWaves + 63) / 64 * 64;
+  const int kb = min(ce, cb + wave * share), ke = min(ce, kb + share);
+  float m, l, acc[EPC];
+  first_token_keys<DT, D>(a, seq, head, k_start, kb, ke, m, l, acc);
+  states[wave][lane][0] = m;
+  states[wave][lane][1] = l;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) states[wave][lane][2 + e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < kSplitWaves; ++w) {
+    float acco[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acco[e] = states[w][lane][2 + e];
+    merge_state<EPC>(m, l, acc, states[w][lane][0], states[w][lane][1], acco);
+  }
+  if (nchunks == 1) {
+    first_token_store<DT, D>(a, seq, head, m, l, acc);
+    return;
+  }
+  const int c = lane % LPK;
+  float* mine = a.ft_partials + (static_cast<size_t>(f) * a.heads + head) * STRIDE;
+  if (lane < LPK) {
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(mine + 4 + c * EPC);
+#pragma unroll
+    for (int v = 0; v < EPC / 4; ++v) dst[v] = f32x4_t{acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]};
+    if (lane == 0) {
+      mine[0] = m;
+      mine[1] = l;
+    }
+  }
+  __threadfence();
+  int32_t* arrivals = a.ft_arrivals + static_cast<size_t>(seq) * a.heads + head;
+  int before = 0;
+  if (lane == 0) before = atomicAdd(arrivals, 1);
+  before = __shfl(before, 0);
+  if (before != nchunks - 1) return;
+  __threadfence();
+  m = kNegInf;
+  l = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int j = 0; j < nchunks; ++j) {
+    const float* st = a.ft_partials + (static_cast<size_t>(first + j) * a.heads + head) * STRIDE;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(st + 4 + c * EPC);
+    float acco[EPC];
+#pragma unroll
+    for (int v = 0; v < EPC / 4; ++v) {
+      const f32x4_t x = src[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acco[4 * v + e] = x[e];
+    }
+    merge_state<EPC>(m, l, acc, st[0], st[1], acco);
+  }
+  first_token_store<DT, D>(a, seq, head, m, l, acc);
+  if (lane == 0) *arrivals = 0;
+}
+
+template <int DT, int D, bool PERSISTENT>
+__global__ __launch_bounds__(64 * kSplitWaves) void attn_first_token_chunk_kernel(const AttnArgs a) {
+  __shared__ float states[kSplitWaves][64][Chunk<DT>::N + 2];
+  int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
+  g = min(g, a.grid_cap);
+  const int tasks = g > 0 ? g * a.heads : 0;
+  auto run = [&](int task) __attribute__((always_inline)) {
+    const int slot = task / a.heads;
+    first_token_chunk_task<DT, D>(a, slot, task - slot * a.heads, states);
+  };
+  if constexpr (PERSISTENT) {
+    __shared__ int mailbox;
+    run_claimed_tasks(tasks, a.task_counter, &mailbox, run);
+  } else {
+    const int task = blockIdx.x;
+    if (task < tasks) run(task);
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_chunked(const AttnArgs& a, int64_t slots, int32_t workers, hipStream_t s) {
+  constexpr int threads = 64 * kSplitWaves;
+  const auto kernel = workers == kStaticGrid ? attn_first_token_chunk_kernel<DT, D, false>
+                                             : attn_first_token_chunk_kernel<DT, D, true>;
+  int64_t width = 0;
+  const hipError_t e = launch_width(kernel, threads, slots * a.heads, workers, &width);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(width)), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
 // Head-parallel form (SPLIT false): task t = slot * head_groups + group,
 // wave w of the workgroup takes head 4 * group + w (256 threads).  Key-split
 // form: task t = slot * heads + head, all kSplitWaves waves on that head.  One task per
@@ -338,8 +458,10 @@ hipError_t launch_dt_d(const AttnArgs& a, int64_t slots, int32_t workers, hipStr
 }
 
 template <int DT, int D>
-hipError_t launch_dt_dd(const AttnArgs& a, bool causal, bool split, int64_t slots, int32_t workers, hipStream_t s) {
-  if (split)
+hipError_t launch_dt_dd(const AttnArgs& a, bool causal, FirstTokenForm form, int64_t slots, int32_t workers,
+                        hipStream_t s) {
+  if (form == FirstTokenForm::kChunked) return launch_chunked<DT, D>(a, slots, workers, s);
+  if (form == FirstTokenForm::kKeySplit)
     return causal ? launch_dt_d<DT, D, true, true>(a, slots, workers, s)
                   : launch_dt_d<DT, D, false, true>(a, slots, workers, s);
   return causal ? launch_dt_d<DT, D, true, false>(a, slots, workers, s)
@@ -347,26 +469,26 @@ hipError_t launch_dt_dd(const AttnArgs& a, bool causal, bool split, int64_t slot
 }
 
 template <int DT>
-hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, bool split, int64_t slots, int32_t workers,
-                     hipStream_t s) {
+hipError_t launch_dt(const AttnArgs& a, int head_dim, bool causal, FirstTokenForm form, int64_t slots,
+                     int32_t workers, hipStream_t s) {
   switch (head_dim) {
-    case 16: return launch_dt_dd<DT, 16>(a, causal, split, slots, workers, s);
-    case 32: return launch_dt_dd<DT, 32>(a, causal, split, slots, workers, s);
-    case 64: return launch_dt_dd<DT, 64>(a, causal, split, slots, workers, s);
-    case 128: return launch_dt_dd<DT, 128>(a, causal, split, slots, workers, s);
+    case 16: return launch_dt_dd<DT, 16>(a, causal, form, slots, workers, s);
+    case 32: return launch_dt_dd<DT, 32>(a, causal, form, slots, workers, s);
+    case 64: return launch_dt_dd<DT, 64>(a, causal, form, slots, workers, s);
+    case 128: return launch_dt_dd<DT, 128>(a, causal, form, slots, workers, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, bool split,
+hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, FirstTokenForm form,
                                    int64_t slots, int32_t workers, hipStream_t s) {
   if (slots <= 0) return hipSuccess;
   switch (dtype) {
-    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, split, slots, workers, s);
-    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, split, slots, workers, s);
-    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, split, slots, workers, s);
+    case VLP_FP32: return launch_dt<VLP_FP32>(a, head_dim, causal, form, slots, workers, s);
+    case VLP_FP16: return launch_dt<VLP_FP16>(a, head_dim, causal, form, slots, workers, s);
+    case VLP_BF16: return launch_dt<VLP_BF16>(a, head_dim, causal, form, slots, workers, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
                                                               int block_m, int32_t* __restrict__ block_offsets,
                                                               int32_t* __restrict__ grid_mapping,
                                                               int32_t* __restrict__ tile_order, int grid_cap,
-                                                              int32_t* __restrict__ task_counter) {
+                                                              int32_t* __restrict__ task_counter,
+                                                              int32_t* __restrict__ zero, int zero_count) {
   __shared__ int len_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int bo_s[VLP_DEVICE_SORT_MAX_SEQS];
   __shared__ int order_s[VLP_DEVICE_SORT_MAX_SEQS];
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
   const int end = min(num_seqs, beg + per);
   const bool sorted = num_seqs <= VLP_DEVICE_SORT_MAX_SEQS;
   if (task_counter && tid < kTaskQueues) task_counter[tid * kCounterStride] = 0;
+  for (int i = tid; i < zero_count; i += kThreads) zero[i] = 0;
 
   // 1. block_offsets and grid_mapping.
   int local = 0;
@@ -217,9 +219,11 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
 
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                              int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
-                             int64_t grid_cap, int32_t* task_counter, hipStream_t s) {
+                             int64_t grid_cap, int32_t* task_counter, hipStream_t s, int32_t* zero,
+                             int32_t zero_count) {
   hipLaunchKernelGGL(grid_build_kernel, dim3(1), dim3(kThreads), 0, s, cu_seqlens, num_seqs, block_m,
-                     block_offsets, grid_mapping, tile_order, static_cast<int>(grid_cap), task_counter);
+                     block_offsets, grid_mapping, tile_order, static_cast<int>(grid_cap), task_counter, zero,
+                     zero ? zero_count : 0);
   return hipGetLastError();
 }
 

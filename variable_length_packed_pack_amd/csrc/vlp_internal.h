@@ -38,6 +38,11 @@ struct AttnArgs {
   int32_t kv_stride;           // k and v
   int32_t o_stride;
   int32_t* task_counter;       // persistent launches: the queue counters (zero at launch)
+  // Chunked first-token form only: per-chunk partial states
+  // [chunks][heads][head_dim + 4] fp32 (m, l, two unused words, acc) and
+  // per-(sequence, head) arrival counters [num_seqs][heads] (zero at launch).
+  float* ft_partials;
+  int32_t* ft_arrivals;
 };
 
 // Arguments of the two backward launches (the dQ kernel over the query
@@ -217,16 +222,30 @@ hipError_t launch_attn_f16(const AttnArgs& a, int head_dim, bool causal, int64_t
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool causal, int64_t blocks,
                            int32_t workers, hipStream_t s);
 
-// First-token forward over `slots` sequences: one wavefront per (sequence,
-// head), or with `split` eight wavefronts per (sequence, head), each on an
-// eighth of the keys (long sequences; see kFirstTokenSplitKeys).
-hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, bool split,
+enum class FirstTokenForm { kHeadParallel, kKeySplit, kChunked };
+
+// First-token forward over `slots` tile slots: one wavefront per (sequence,
+// head); or eight wavefronts per (sequence, head), each on an eighth of the
+// keys (long sequences; see kFirstTokenSplitKeys); or, chunked, eight
+// wavefronts per (chunk of kFirstTokenChunkKeys keys, head) with the grid
+// built over the keys in chunks.
+hipError_t launch_attn_first_token(int dtype, const AttnArgs& a, int head_dim, bool causal, FirstTokenForm form,
                                    int64_t slots, int32_t workers, hipStream_t s);
 
 // First-token launches split each sequence's keys over eight wavefronts when
 // the longest sequence (max_seqlen, or the mean length when no hint is
 // given) has at least this many keys.
 constexpr int64_t kFirstTokenSplitKeys = 1024;
+
+// With a workspace (the device-grid entry points) and at least this many
+// keys in the longest sequence, first-token launches take the chunked form:
+// a grid over the keys with kFirstTokenChunkKeys keys per tile, one
+// workgroup per (chunk, head), the partial states of a sequence merged by
+// the workgroup that finishes last.
+constexpr int64_t kFirstTokenChunkKeys = VLP_FIRST_TOKEN_CHUNK_KEYS;
+constexpr int64_t kFirstTokenChunkMin = VLP_FIRST_TOKEN_CHUNK_MIN;
+static_assert(kFirstTokenChunkKeys % 512 == 0, "a chunk splits into 64-key shares of eight waves");
+static_assert(kFirstTokenChunkMin >= kFirstTokenChunkKeys, "a chunked launch has sequences of several chunks");
 
 // Backward launches over `blocks` tasks each.
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, int head_dim, bool causal, int64_t blocks,
@@ -265,9 +284,11 @@ hipError_t noalloc_scratch(void** ptr);
 
 // Device ragged-grid build (one workgroup); also zeroes the kTaskQueues
 // counters at task_counter (kCounterStride apart) when it is not null (the
-// work queues of the persistent launch that follows).
+// work queues of the persistent launch that follows), and zero_count ints
+// at `zero` (counters of the launch that follows).
 hipError_t launch_grid_build(const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_m,
                              int32_t* block_offsets, int32_t* grid_mapping, int32_t* tile_order,
-                             int64_t grid_cap, int32_t* task_counter, hipStream_t s);
+                             int64_t grid_cap, int32_t* task_counter, hipStream_t s, int32_t* zero = nullptr,
+                             int32_t zero_count = 0);
 
 }  // namespace vlp
