@@ -260,8 +260,9 @@ vlp_status vlp_varlen_attn_fwd_workspace_size(int32_t dtype, int32_t num_seqs, i
  *                  views).  Each must be >= heads * head_dim, give 16-byte
  *                  aligned rows, and stride * element size <= 2^24 bytes.
  *   max_seqlen     a hint (0 = unknown); never needed for correctness.
- *   scale          finite softmax scale >= 0 (usually 1/sqrt(head_dim)); the
- *                  running row maximum is taken on the unscaled scores.
+ *   scale          any finite softmax scale (usually 1/sqrt(head_dim)).  A
+ *                  negative scale runs as |scale| with q's sign flipped in
+ *                  the score products (scale * s = |scale| * (-s)).
  *   causal         0/1: key j of a sequence is visible to its query at local
  *                  position p iff j <= p + (Lk - Lq) (bottom-right aligned).
  *   query_is_first_token  0/1: one query per sequence, at local position 0.
@@ -275,7 +276,7 @@ vlp_status vlp_varlen_attn_fwd_workspace_size(int32_t dtype, int32_t num_seqs, i
  * Errors: NULL q/k/v/out/cu_seqlens_k/workspace (or cu_seqlens_q outside
  * first-token mode) -> VLP_ERR_NULL; dtype or head_dim not built ->
  * VLP_ERR_UNSUPPORTED; num_seqs < 1, heads < 1, rows_q < 0, total_k < 0,
- * non-finite or negative scale, misaligned pointers, a stride below heads *
+ * non-finite scale, misaligned pointers, a stride below heads *
  * head_dim or not giving 16-byte aligned rows, rows_q != num_seqs in
  * first-token mode -> VLP_ERR_INVALID; rows or rows*heads beyond int32, a
  * stride beyond 2^24 bytes -> VLP_ERR_OVERFLOW; small workspace ->

@@ -315,7 +315,8 @@ def test_forward_validation_errors():
     assert _fwd(rows_q=-1) == 2
     assert _fwd(scale=float("nan")) == 2
     assert _fwd(scale=float("inf")) == 2
-    assert _fwd(scale=-0.125) == 2  # the online max assumes a non-negative scale
+    assert _fwd(scale=-0.125, ws_bytes=16) == 4  # any finite scale passes (runs as |scale| on -q)
+    assert _fwd(scale=-0.0, ws_bytes=16) == 4
     assert _fwd(scale=0.0) != 2
     assert _fwd(q=FAKE + 8) == 2
     assert _fwd(out=FAKE + 4) == 2
@@ -375,7 +376,7 @@ def test_backward_validation_errors():
     assert _bwd(heads=0) == 2
     assert _bwd(total_k=-1) == 2
     assert _bwd(scale=float("nan")) == 2
-    assert _bwd(scale=-1.0) == 2
+    assert _bwd(scale=-1.0, ws_bytes=16) == 4  # any finite scale passes validation
     assert _bwd(causal=3) == 2
     for name in ("dout", "dq", "dk", "dv"):
         assert _bwd(**{name: FAKE + 8}) == 2, name

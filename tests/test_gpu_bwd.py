@@ -179,6 +179,32 @@ def test_bwd_cross_lengths_keyless_queries_and_unowned_rows():
                 assert (g[0][s5] == 0).all()
 
 
+@pytest.mark.parametrize("dtype,head_dim", [("fp32", 64), ("bf16", 128), ("fp16", 64), ("bf16", 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_negative_scale(dtype, head_dim, causal):
+    """Gradients under a negative softmax scale against the oracle, and their
+    relation to the positive scale on negated queries: dq(q, -s) = -dq(-q, s)
+    and dv equal bit for bit (the kernels run |s| with the resident operand of
+    the score products negated, so both runs feed the matrix cores the same
+    values); dk(q, -s) sums dS q where the other run sums dS (-q), and the
+    matrix cores' fp32 accumulation is not symmetric under negation to the
+    last bit, so dk agrees to a few ulp."""
+    lengths = [1, 70, 300, 129, 65]
+    scale = -1.5 / math.sqrt(head_dim)
+    wl = workloads.custom_workload(lengths, 2, head_dim, dtype, causal, seed=31 + head_dim)
+    dout = workloads.random_dout(wl.total_tokens, 2, head_dim, dtype, seed=32 + head_dim)
+    cu = _cu(lengths)
+    dq, dk, dv = _check_all(wl.q, wl.k, wl.v, dout, cu, cu, scale, causal, dtype, "negative scale")
+    dq2, dk2, dv2 = _run(-wl.q, wl.k, wl.v, dout, cu, cu, -scale, causal)
+    for name, a, b in (("dq", dq, -dq2), ("dk", dk, dk2), ("dv", dv, dv2)):
+        n = int(np.sum(a != b))
+        _say(f"[bwd]   {name}: {n} elements differ from the negated-query run, max {np.max(np.abs(a - b)):.3e}")
+        if name == "dk":
+            assert np.all(np.abs(a - b) <= 2.0 ** -6 * np.abs(b) + 1e-6)
+        else:
+            assert n == 0
+
+
 def test_bwd_zero_scale():
     """scale = 0: uniform weights; dq and dk are exactly zero."""
     lengths = [1, 70, 129, 5]

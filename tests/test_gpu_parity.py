@@ -372,6 +372,40 @@ def test_zero_scale_gives_uniform_weights(dtype):
         assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= TOL_LSE
 
 
+@pytest.mark.parametrize("dtype", EDGE_DTYPES)
+@pytest.mark.parametrize("head_dim", [16, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_scale(dtype, head_dim, causal):
+    """A negative softmax scale (the definition holds for any real scale)
+    against the oracle, and bit-identical to the positive scale on negated
+    queries: the kernels run |scale| on -q, an exact rewrite."""
+    lengths = [1, 70, 300, 129, 5, 257]
+    scale = -1.5 / math.sqrt(head_dim)
+    wl = workloads.custom_workload(lengths, 2, head_dim, dtype, causal, seed=17 + head_dim)
+    q, k, v, cu_d, cu_h = _to_dev(wl)
+    out, lse = vlp.varlen_attn_fwd(q, k, v, cu_d, cu_d, 0, scale, causal)
+    out2, lse2 = vlp.varlen_attn_fwd(-q, k, v, cu_d, cu_d, 0, -scale, causal)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.varlen_attention(wl.q, wl.k, wl.v, cu_h.numpy(), cu_h.numpy(), scale, causal)
+    err = np.max(np.abs(out.float().cpu().numpy() - ref))
+    lerr = np.max(np.abs(lse.cpu().numpy() - ref_lse))
+    _say(f"[parity] negative scale {dtype} D={head_dim} causal={causal}: out {err:.3e} lse {lerr:.3e}")
+    assert err <= TOL_OUT[dtype] and lerr <= TOL_LSE
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # first-token mode, each form: head-parallel, key split, chunked
+    for ft_lengths, hint in (([1, 70, 300, 5], 300), ([1500, 3, 1100], 1500), ([9000, 20, 4097], 9000)):
+        wf = workloads.custom_workload(ft_lengths, 2, head_dim, dtype, False, seed=19 + head_dim)
+        cu = wf.cu_seqlens_host()
+        qf = wf.q[torch.from_numpy(cu[:-1]).long()].contiguous()
+        cud = torch.from_numpy(cu).to(DEV)
+        for c in (False, True):
+            o, l = vlp.varlen_attn_fwd(qf.to(DEV), wf.k.to(DEV), wf.v.to(DEV), None, cud, hint, scale, c, True)
+            torch.cuda.synchronize()
+            r, rl = oracle.varlen_attention(qf, wf.k, wf.v, None, cu, scale, c, query_is_first_token=True)
+            assert np.max(np.abs(o.float().cpu().numpy() - r)) <= TOL_OUT[dtype]
+            assert np.max(np.abs(l.cpu().numpy() - rl)) <= TOL_LSE
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_strided_views_of_a_fused_projection(dtype, head_dim):

@@ -96,7 +96,7 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
   if (!vlp::head_dim_built(head_dim)) return VLP_ERR_UNSUPPORTED;
   if (num_seqs < 1 || heads < 1 || rows_q < 0 || total_k < 0 || max_seqlen < 0) return VLP_ERR_INVALID;
   if ((causal != 0 && causal != 1) || (first_token != 0 && first_token != 1)) return VLP_ERR_INVALID;
-  if (!isfinite(scale) || scale < 0.0f) return VLP_ERR_INVALID;  // the online max assumes scale >= 0
+  if (!isfinite(scale)) return VLP_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VLP_ERR_INVALID;
   if (first_token && rows_q != num_seqs) return VLP_ERR_INVALID;
   if (rows_q > INT32_MAX || total_k > INT32_MAX) return VLP_ERR_OVERFLOW;
@@ -115,7 +115,13 @@ vlp_status check_forward(int32_t dtype, const void* q, const void* k, const void
 // map to -inf, which -inf * 0 would not: a zero scale is replaced by the
 // smallest normal float, which leaves every finite score at (nearly) 0, so
 // exp2 returns exactly 1 and the weights are exactly uniform, as for scale 0.
-float exp2_factor(float scale) { return scale > 0.0f ? scale * 1.4426950408889634f : 1.17549435e-38f; }
+// A negative scale runs as |scale| with the register-resident operand of the
+// score products negated (negate_q / negate), which keeps every kernel's
+// running maximum order-preserving: scale * s = |scale| * (-s).
+float exp2_factor(float scale) {
+  const float mag = fabsf(scale);
+  return mag > 0.0f ? mag * 1.4426950408889634f : 1.17549435e-38f;
+}
 
 vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
                         int32_t num_seqs, int64_t rows_q, int32_t heads, float scale, void* out, float* lse,
@@ -136,6 +142,7 @@ vlp::AttnArgs make_args(const void* q, const void* k, const void* v, const int32
   a.rows_q = static_cast<int32_t>(rows_q);
   a.num_blocks = -1;
   a.scale_log2 = exp2_factor(scale);
+  a.negate_q = scale < 0.0f ? 1 : 0;
   return a;
 }
 
@@ -543,6 +550,7 @@ vlp::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const vo
   a.rows_q = static_cast<int32_t>(rows_q);
   a.scale = scale;
   a.scale_log2 = exp2_factor(scale);
+  a.negate = scale < 0.0f ? 1 : 0;
   return a;
 }
 

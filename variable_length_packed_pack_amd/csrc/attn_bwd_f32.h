@@ -152,6 +152,8 @@ __device__ __forceinline__ void attn_bwd_dq_f32_task(const BwdArgs& a, int task,
 #pragma unroll
     for (int j = 0; j < HALF / 4; ++j) {
       qv[j] = *reinterpret_cast<const f32x4_t*>(qp + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[j][e] = flip_sign(qv[j][e], a.negate);
       dov[j] = *reinterpret_cast<const f32x4_t*>(dop + 4 * j);
       const f32x4_t ov = *reinterpret_cast<const f32x4_t*>(op + 4 * j);
 #pragma unroll
@@ -307,6 +309,8 @@ __device__ __forceinline__ void attn_bwd_dkdv_f32_task(const BwdArgs& a, int tas
 #pragma unroll
     for (int j = 0; j < HALF / 4; ++j) {
       kv[j] = *reinterpret_cast<const f32x4_t*>(kp + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[j][e] = flip_sign(kv[j][e], a.negate);
       vv[j] = *reinterpret_cast<const f32x4_t*>(vp + 4 * j);
     }
   }

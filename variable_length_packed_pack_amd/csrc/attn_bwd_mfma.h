@@ -273,6 +273,8 @@ __device__ __forceinline__ void attn_bwd_dq_h16_task(const BwdArgs& a, int task,
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[k][j] = flip_sign16x2(qv[k][j], a.negate);
       dov[k] = *reinterpret_cast<const u32x4_t*>(dop + 16 * k + 8 * hh);
       const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(op + 16 * k + 8 * hh);
 #pragma unroll
@@ -433,6 +435,8 @@ __device__ __forceinline__ void attn_bwd_dkdv_h16_task(const BwdArgs& a, int tas
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       kv[k] = *reinterpret_cast<const u32x4_t*>(kp + 16 * k + 8 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kv[k][j] = flip_sign16x2(kv[k][j], a.negate);
       vv[k] = *reinterpret_cast<const u32x4_t*>(vp + 16 * k + 8 * hh);
     }
   }

@@ -151,6 +151,8 @@ __device__ __forceinline__ void first_token_keys(const AttnArgs& a, int seq, int
     const char* qp = static_cast<const char*>(a.q) +
                      (static_cast<size_t>(seq) * a.q_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);
     C::widen(*reinterpret_cast<const u32x4_t*>(qp), qf);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qf[e] = flip_sign(qf[e], a.negate_q);
   }
   const size_t kv_off =
       (static_cast<size_t>(k_start) * a.kv_stride + static_cast<size_t>(head) * D + c * EPC) * (16 / EPC);

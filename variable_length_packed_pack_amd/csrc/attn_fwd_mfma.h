@@ -303,7 +303,11 @@ __device__ __forceinline__ void attn_fwd_h16_task(const AttnArgs& a, int task, c
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(tc.q_start + qrow) * a.q_stride +
                          static_cast<size_t>(tc.head) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
+    for (int k = 0; k < KS; ++k) {
+      qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[k][j] = flip_sign16x2(qv[k][j], a.negate_q);
+    }
   }
 
   // Direct-load lane offsets (bytes, relative to the key block's first row):
@@ -559,7 +563,11 @@ __device__ __forceinline__ void attn_fwd_f32_task(const AttnArgs& a, int task, c
     const float* qp = static_cast<const float*>(a.q) + static_cast<size_t>(tc.q_start + qrow) * a.q_stride +
                       static_cast<size_t>(tc.head) * D + hh * HALF;
 #pragma unroll
-    for (int j = 0; j < HALF / 4; ++j) qv[j] = *reinterpret_cast<const f32x4_t*>(qp + 4 * j);
+    for (int j = 0; j < HALF / 4; ++j) {
+      qv[j] = *reinterpret_cast<const f32x4_t*>(qp + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[j][e] = flip_sign(qv[j][e], a.negate_q);
+    }
   }
 
   // Direct-load lane offsets (see the 16-bit path).

@@ -109,7 +109,11 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(tc.q_start + qrow) * a.q_stride +
                          static_cast<size_t>(tc.head) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
+    for (int k = 0; k < KS; ++k) {
+      qv[k] = *reinterpret_cast<const u32x4_t*>(qp + 16 * k + 8 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[k][j] = flip_sign16x2(qv[k][j], a.negate_q);
+    }
   }
 
   int voff[LPW];

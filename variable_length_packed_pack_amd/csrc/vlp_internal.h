@@ -30,7 +30,8 @@ struct AttnArgs {
   int32_t rows_q;
   int32_t num_blocks;          // G when known on the host, -1: read block_offsets[num_seqs]
   int32_t grid_cap;            // entries of grid_mapping / tile_order (guards bad metadata)
-  float scale_log2;            // scale * log2(e): scores go straight to exp2
+  float scale_log2;            // |scale| * log2(e): scores go straight to exp2
+  int32_t negate_q;            // 1 when scale < 0: q enters the products negated (see api.cpp)
   // Elements between consecutive tokens (a head's D elements are contiguous
   // and heads are D apart): heads * head_dim for contiguous tensors, more for
   // views into a fused projection output.
@@ -69,7 +70,9 @@ struct BwdArgs {
   int32_t rows_q;
   int32_t grid_cap;
   float scale;                 // factor of dq and dk
-  float scale_log2;            // scores -> exp2 units
+  float scale_log2;            // |scale| * log2(e): scores -> exp2 units
+  int32_t negate;              // 1 when scale < 0: the register-resident q (dq kernel) or k (dk/dv kernel)
+                               // enters the score products negated
   // Elements between consecutive tokens, as in AttnArgs.
   int32_t q_stride;
   int32_t kv_stride;           // k and v
@@ -190,6 +193,14 @@ __device__ __forceinline__ void run_claimed_tasks(int tasks, int32_t* counters, 
     __syncthreads();  // and read by every wave before the LDS is reused
   }
 }
+
+// Sign flip of an operand held in registers, for a negative softmax scale:
+// scale * (q . k) = |scale| * ((-q) . k) -- the flip negates every product
+// exactly, and the sums differ from -(q . k) at most by the accumulation's
+// rounding -- so the kernels run with |scale| and keep their running
+// maximum order-preserving.  Two 16-bit values per 32-bit word.
+__device__ __forceinline__ uint32_t flip_sign16x2(uint32_t x, bool on) { return on ? x ^ 0x80008000u : x; }
+__device__ __forceinline__ float flip_sign(float x, bool on) { return on ? -x : x; }
 
 // threadIdx.x behind an empty asm statement.  The task functions of the
 // task-looping kernels derive their lane offsets from it, so those offsets
