@@ -119,6 +119,22 @@ def traffic_from_profile(workload: str, src_hash: str, kernel: str = "attn_fwd")
     return rec.get("hbm_bytes_per_launch")
 
 
+def trace_of_bench(workload: str, build: str, kernel: str = "attn_fwd"):
+    """The committed rocprofv3 kernel trace of this very command (bench.py on
+    the same workload, profiled), or None unless it was taken with the
+    library build loaded now: its average attention-kernel duration gives the
+    trace-derived roofline fraction reported next to the HIP-event one."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_bench_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("library_build") != build:
+        return None
+    rec["path"] = os.path.relpath(path, ROOT)
+    return rec
+
+
 def cpu_oracle_baseline(wl, budget_s: float, first_token: bool = False):
     """Time the oracle on a bounded sample of the same batch: whole heads (every
     sequence of the batch for that head), one after another, until the
@@ -973,6 +989,17 @@ def main() -> int:
         src_hash = kernel_source_hash(KERNEL_SOURCES_F32 if wl.dtype == "fp32" else KERNEL_SOURCES)
         traffic = traffic_from_profile(args.workload, src_hash)
     log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
+    trace = trace_of_bench(args.workload + ("_first_token" if ft else ""), vlp.build_info(),
+                           kernel="attn_first_token" if ft else "attn_fwd")
+    if trace is not None and not ft:
+        # the same roofline from the profiled run of this command: per-launch
+        # algorithmic flops over the trace's average kernel duration
+        t_us = trace["timed_loop_avg_us"]
+        roof["trace"] = {"source": trace["path"], "kernel_avg_us": t_us,
+                         "achieved": round(flops / (t_us * 1e-6) / 1e12, 3),
+                         "frac": round(flops / (t_us * 1e-6) / 1e12 / roof["peak"], 4),
+                         "profiled_run": {"kernel_ms": trace["bench_kernel_ms"],
+                                          "ms_per_step": trace["bench_ms_per_step"]}}
 
     padded_ms, padded_backend = (None, "skipped")
     envelope_ms = None

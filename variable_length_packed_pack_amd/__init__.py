@@ -104,21 +104,24 @@ def check_library_current() -> str:
 def pack_sequences(lengths, max_seq_len: int):
     """lengths (host, int) -> (flat_index int64 [T], cu_seqlens int32 [B+1]), CPU tensors."""
     lib = _lib.load()
-    lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64).reshape(-1))
-    if lens.size and (lens.min() < -2**31 or lens.max() > 2**31 - 1):
-        raise _lib.VlpError(_lib.VLP_ERR_INVALID, "pack_sequences")
-    lens = lens.astype(np.int32)
+    lens = np.asarray(lengths)
+    if lens.dtype != np.int32:
+        wide = lens.astype(np.int64).reshape(-1)
+        if wide.size and (wide.min() < -2**31 or wide.max() > 2**31 - 1):
+            raise _lib.VlpError(_lib.VLP_ERR_INVALID, "pack_sequences")
+        lens = wide.astype(np.int32)
+    lens = np.ascontiguousarray(lens.reshape(-1))
     b = int(lens.size)
-    cu = np.zeros(b + 1, dtype=np.int32)
+    cu = np.empty(b + 1, dtype=np.int32)
     total = ctypes.c_int64(0)
-    st = lib.vlp_pack_sequences(lens.ctypes.data, b, int(max_seq_len), None, 0, cu.ctypes.data,
+    # One call: the buffer is sized by the lengths' sum; the library validates
+    # the lengths (and the sum) and fills both outputs, or reports the error.
+    cap = int(lens.sum(dtype=np.int64)) if b else 0
+    flat = np.empty(max(cap, 1), dtype=np.int64)
+    st = lib.vlp_pack_sequences(lens.ctypes.data, b, int(max_seq_len), flat.ctypes.data, cap, cu.ctypes.data,
                                 ctypes.addressof(total))
     _lib.check(st, "pack_sequences")
-    flat = np.zeros(max(total.value, 1), dtype=np.int64)
-    st = lib.vlp_pack_sequences(lens.ctypes.data, b, int(max_seq_len), flat.ctypes.data, total.value,
-                                cu.ctypes.data, ctypes.addressof(total))
-    _lib.check(st, "pack_sequences")
-    return torch.from_numpy(flat[: total.value].copy()), torch.from_numpy(cu)
+    return torch.from_numpy(flat if cap else flat[:0]), torch.from_numpy(cu)
 
 
 def grid_capacity(total_tokens: int, num_seqs: int, block_m: int) -> int:

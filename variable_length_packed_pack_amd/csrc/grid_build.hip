@@ -16,7 +16,7 @@
 //      they are compacted first (a scan of the non-empty flags), so a launch
 //      sized for a sequence capacity far above M -- a zero-length tail of
 //      capacity slots -- orders M keys, not the capacity.  For up to kRankMax
-//      of them every sequence counts the sequences that precede it; above
+//      of them every sequence counts the larger keys (len << 32 | ~i); above
 //      that, a bitonic sort in LDS of the keys ((INT32_MAX - len) << 32 | i);
 //   3. a second prefix sum of tile counts in that order gives every
 //      sequence's position in tile_order; each slot is filled by its own
@@ -142,16 +142,23 @@ __global__ __launch_bounds__(kThreads) void grid_build_kernel(const int32_t* __r
     if (len_s[i] > 0) pos_s[at++] = i;
   __syncthreads();
   if (m <= kRankMax) {
+    // One 64-bit key per non-empty sequence, larger for an earlier place
+    // (length in the high word, the complement of the index below it, so
+    // equal lengths keep index order); a sequence's rank is the number of
+    // larger keys.  Every thread reads the same key in each step (an LDS
+    // broadcast), and the loads are independent of one another.
     for (int a = tid; a < m; a += kThreads) {
       const int i = pos_s[a];
-      const int li = len_s[i];
+      keys[a] = (static_cast<unsigned long long>(static_cast<unsigned>(len_s[i])) << 32) |
+                (0xffffffffu - static_cast<unsigned>(i));
+    }
+    __syncthreads();
+    for (int a = tid; a < m; a += kThreads) {
+      const unsigned long long ka = keys[a];
       int rank = 0;
-      for (int b = 0; b < m; ++b) {
-        const int j = pos_s[b];
-        const int lj = len_s[j];
-        rank += (lj > li) || (lj == li && j < i);
-      }
-      order_s[rank] = i;
+#pragma unroll 8
+      for (int b = 0; b < m; ++b) rank += keys[b] > ka;
+      order_s[rank] = static_cast<int>(0xffffffffu - static_cast<unsigned>(ka & 0xffffffffu));
     }
   } else {
     int p2 = 1;
