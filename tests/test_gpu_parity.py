@@ -318,6 +318,36 @@ def test_scores_that_outgrow_the_running_max(dtype, head_dim, causal, profile):
     _check_full(wl)
 
 
+@pytest.mark.parametrize("heads,head_dim,dtype", [(32, 16, "bf16"), (64, 64, "fp16"), (32, 128, "bf16"),
+                                                   (32, 64, "fp32"), (40, 32, "bf16")])
+def test_many_heads_task_order(heads, head_dim, dtype):
+    """Head counts that are multiples of 32 run each XCD's heads one after
+    another (the other counts interleave them): every (tile, head) still runs
+    exactly once -- static grid, persistent schedule with several worker
+    counts and cached grid give the same bits, and match the oracle."""
+    lengths = [300, 1, 129, 70, 513, 2]
+    wl = workloads.custom_workload(lengths, heads, head_dim, dtype, True, seed=heads + head_dim)
+    q, k, v, cu_d, cu_h = _to_dev(wl)
+    out, lse = vlp.varlen_attn_fwd(q, k, v, cu_d, cu_d, 0, wl.scale, True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.varlen_attention(wl.q, wl.k, wl.v, cu_h.numpy(), cu_h.numpy(), wl.scale, True)
+    err = np.max(np.abs(out.float().cpu().numpy() - ref))
+    lerr = np.max(np.abs(lse.cpu().numpy() - ref_lse))
+    _say(f"[parity] {heads} heads {dtype} D={head_dim}: out {err:.3e} lse {lerr:.3e}")
+    assert err <= TOL_OUT[dtype] and lerr <= TOL_LSE
+    for nw in (0, 3, 8, 37):
+        o2, l2 = vlp.varlen_attn_fwd(q, k, v, cu_d, cu_d, 0, wl.scale, True, num_workers=nw)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out) and torch.equal(l2, lse), nw
+    bm = vlp.kernel_block_m(q.dtype, head_dim, True)
+    host = vlp.build_ragged_grid(cu_h, bm)
+    g = vlp.RaggedGrid(host.grid_mapping.to(DEV), host.block_offsets.to(DEV), host.tile_order.to(DEV),
+                       host.num_blocks, bm)
+    o3, l3 = vlp.varlen_attn_fwd(q, k, v, cu_d, cu_d, 0, wl.scale, True, grid=g)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, out) and torch.equal(l3, lse)
+
+
 @pytest.mark.parametrize("dtype", EDGE_DTYPES)
 def test_single_long_sequence(dtype):
     wl = workloads.custom_workload([1000], 2, 64, dtype, False, seed=11)

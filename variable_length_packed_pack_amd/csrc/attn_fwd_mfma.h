@@ -111,11 +111,32 @@ __device__ __forceinline__ int active_tasks(const AttnArgs& a) {
   return g > 0 ? g * a.heads : 0;
 }
 
-// Task t (< active_tasks) is head t % heads of tile slot t / heads.
+// Task t (< active_tasks) -> (tile slot, head).  The hardware deals
+// workgroup t to XCD t % 8 and starts each XCD's workgroups in order (the
+// persistent schedule's per-XCD queues keep that), so the decode decides
+// which tiles share an XCD's L2 at a time.  Task t is head t % heads of slot
+// t / heads -- each XCD interleaves its heads x, x + 8, ... slot by slot --
+// except when an XCD has four or more heads (heads a multiple of 32): then
+// it runs them one after another, each head's slots in longest-first order,
+// so that the tiles resident on an XCD stream one head's K/V.  Measured on
+// the skewed batch (32 heads): HBM reads 6.8 -> 5.5 GB per launch, kernel
+// 3 % faster; on 16 heads the same order was 1.5 % slower, so two heads per
+// XCD stay interleaved.
 __device__ __forceinline__ bool decode_task(const AttnArgs& a, int task, TileCoord& tc) {
   const int heads = a.heads;
-  const int slot = task / heads;
-  tc.head = task - slot * heads;
+  int slot;
+  if ((heads & 31) == 0) {
+    int g = a.num_blocks >= 0 ? a.num_blocks : a.block_offsets[a.num_seqs];
+    g = min(g, a.grid_cap);
+    if (g <= 0) return false;
+    const int i = task >> 3;
+    const int j = i / g;
+    slot = i - j * g;
+    tc.head = (task & 7) + 8 * j;
+  } else {
+    slot = task / heads;
+    tc.head = task - slot * heads;
+  }
   const int f = a.tile_order ? a.tile_order[slot] : slot;
   if (f < 0 || f >= a.grid_cap) return false;  // out-of-contract metadata: skip, never read past it
   tc.seq = a.grid_mapping[f];
