@@ -820,6 +820,10 @@ def main() -> int:
     ap.add_argument("--overcapture", default=None, metavar="R1,R2,...",
                     help="graph replays captured for R times the workload's token and sequence capacity, "
                          "static grid against persistent schedule (with --backward: forward and gradients)")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="only time a 4 GiB device-to-device copy (torch) and print the achieved bandwidth: the "
+                         "streaming rate a plain library kernel reaches on this GPU, beside the 8 TB/s datasheet "
+                         "peak that the HBM-bound rooflines are quoted against")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: the "
                          "reference point that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -839,6 +843,24 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    if args.hbm_reference:
+        nbytes = 4 << 30
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"hbm_reference": "torch device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "ms": round(ms, 4), "GB_per_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(2 * nbytes / (ms * 1e-3) / 8e12, 4)}), flush=True)
+        return 0
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)

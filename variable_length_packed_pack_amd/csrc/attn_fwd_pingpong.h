@@ -10,27 +10,31 @@
 //
 //  * eight waves, 256 query rows per tile: waves 0-3 (group 0) and 4-7
 //    (group 1), one wave of each group on every SIMD;
-//  * time is cut into slots separated by workgroup barriers.  A wave's work
-//    on key block j alternates between an MFMA phase M(j) -- PV of block
-//    j-1, then QK^T of block j -- and a VALU phase V(j) -- mask, online
-//    softmax and the bf16/fp16 packing of P_j.  Group 0 runs M(j) in slot 2j
-//    and V(j) in slot 2j+1; group 1 runs the same one slot later.  In every
-//    slot each SIMD therefore holds one wave issuing MFMAs and one wave doing
-//    exponentials, instead of two waves that may want the same unit at once;
-//    the MFMA-phase wave also runs at raised issue priority;
+//  * a wave's work on key block j alternates between an MFMA phase M(j) --
+//    PV of block j-1, then QK^T of block j -- and a VALU phase V(j) -- mask,
+//    online softmax and the bf16/fp16 packing of P_j.  Group 0 runs M(j),
+//    V(j) in period j; group 1 runs V(j-1), M(j).  So while group 0 issues
+//    MFMAs group 1 does exponentials and the other way round: each SIMD holds
+//    one wave of each kind instead of two waves that want the same unit at
+//    once, and the MFMA-phase wave runs at raised issue priority.  Periods
+//    end at a workgroup barrier; inside a period the two phases of the groups
+//    settle into step by themselves (a barrier between them as well, forcing
+//    the alternation, measured 0.5 % slower on the Zipf batch and 2 % on the
+//    skewed one: it added the waves' skew twice per block);
 //  * K and V tiles of 64 keys live in a ring of three LDS slots each, filled
-//    by direct buffer-to-LDS loads.  In slot 2i every wave issues its share
-//    of K_{i+2} and V_{i+1}; both are first read in slot 2i+4, and each wave
-//    waits for them (vmcnt, counting only older loads) at the end of slot
-//    2i+3, before the barrier that publishes them.  A ring slot is refilled
-//    only after both groups have finished reading it.  Blocks past the
-//    sequence's last key get an empty buffer descriptor: those loads read no
-//    memory and write zeros into a ring slot that is not used, so every wave
-//    issues the same number of loads in every slot and the vmcnt bound is a
+//    by direct buffer-to-LDS loads.  In period i every wave issues its share
+//    of K_{i+2} and V_{i+1}; both are first read in period i+2, and each wave
+//    waits for them (vmcnt, counting only the newer loads) at the end of
+//    period i+1, before the barrier that publishes them.  A ring slot is
+//    refilled only after the barrier that ends its last reads (K_{i-1} and
+//    V_{i-2} are last read in period i-1).  Blocks past the sequence's last
+//    key get an empty buffer descriptor: those loads read no memory and
+//    write zeros into a ring slot that is not used, so every wave issues the
+//    same number of loads in every period and the vmcnt bound is a
 //    constant;
 //  * every barrier is reached by all eight waves the same number of times
-//    (2 * nblocks + 3 per task, nblocks uniform over the workgroup); waves
-//    whose rows see fewer keys (causal) skip the MFMA and VALU work of those
+//    (nblocks + 2 per task, nblocks uniform over the workgroup); waves whose
+//    rows see fewer keys (causal) skip the MFMA and VALU work of those
 //    blocks but not the barriers or the loads.
 #pragma once
 
@@ -237,10 +241,10 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
         for (int jj = 0; jj < 4; ++jj) p[i][kk][jj] = E::pack2(s[i][8 * kk + 2 * jj], s[i][8 * kk + 2 * jj + 1]);
   };
 
-  // Loads of slot pair i, issued in the even slot 2i by every wave: K_{i+2}
-  // and V_{i+1} (R = i % 3 names the ring slots statically).  They may still
-  // be in flight at the end of slot 2i+1; everything older has landed by
-  // then (wait_older), in time for the blocks' first use in slot 2i+4.
+  // Loads of period i, issued by every wave: K_{i+2} and V_{i+1} (R = i % 3
+  // names the ring slots statically).  They may still be in flight at the
+  // end of period i; everything older has landed by then (wait_older), in
+  // time for the blocks' first use in period i+2.
   auto issue_pair = [&](auto rr, int i) {
     constexpr int R = decltype(rr)::value;
     issue(kseq, i + 2, kr[(R + 2) % NBUF]);
@@ -256,8 +260,8 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
   wait_vmem_all();
   wg_barrier();
   if (nblocks > 0) {
-    // Group 0 runs M(j) in slot 2j and V(j) in slot 2j+1; group 1 runs the
-    // same one slot later.  M(j) = PV of block j-1, then QK of block j.
+    // Period j: group 0 runs M(j), V(j); group 1 runs V(j-1), M(j).  M(j) =
+    // PV of block j-1, then QK of block j.  One barrier ends each period.
     auto mphase = [&](auto rr, int j) {
       constexpr int R = decltype(rr)::value;
       __builtin_amdgcn_s_setprio(1);
@@ -269,7 +273,6 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
       auto body = [&](auto rr, int j) {
         mphase(rr, j);
         issue_pair(rr, j);
-        wg_barrier();
         if (j < wave_nb) softmax(j);
         wait_older();
         wg_barrier();
@@ -283,17 +286,15 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
       }
       wg_barrier();
     } else {
-      issue_pair(std::integral_constant<int, 0>{}, 0);  // slot 0: idle
-      wg_barrier();
-      mphase(std::integral_constant<int, 0>{}, 0);  // slot 1
+      issue_pair(std::integral_constant<int, 0>{}, 0);  // period 0: M(0) only
+      mphase(std::integral_constant<int, 0>{}, 0);
       wait_older();
       wg_barrier();
-      // V(j) in slot 2j+2 (with the loads of pair j+1), M(j+1) in slot 2j+3.
+      // Period j+1: the loads of period j+1, V(j), M(j+1).
       auto body = [&](auto rr, int j) {
         constexpr int R = decltype(rr)::value;
         issue_pair(std::integral_constant<int, (R + 1) % NBUF>{}, j + 1);
         if (j < wave_nb) softmax(j);
-        wg_barrier();
         mphase(std::integral_constant<int, (R + 1) % NBUF>{}, j + 1);
         wait_older();
         wg_barrier();
@@ -309,7 +310,7 @@ __device__ __forceinline__ void attn_fwd_pingpong_task(const AttnArgs& a, int ta
     }
   }
 
-  // The last slots' loads (empty blocks past the end) may still be writing
+  // The last periods' loads (empty blocks past the end) may still be writing
   // LDS; none may outlive the task (the persistent grid reuses the ring).
   wait_vmem_all();
 
