@@ -117,6 +117,22 @@ def test_device_grid_fuzz_with_ties_and_empty_tails(seed):
         assert np.array_equal(g.tile_order.cpu().numpy()[:len(to)], to)
 
 
+@pytest.mark.parametrize("b", [1, 2, 63, 64, 65, 127, 1023, 1024, 1025, 2048, 3071, vlp.VLP_DEVICE_SORT_MAX_SEQS])
+def test_device_grid_order_at_sort_sizes(b):
+    """Longest-first order at sequence counts on both sides of the sort's
+    power-of-two and per-thread boundaries, every sequence non-empty, with
+    heavy ties."""
+    rng = np.random.default_rng(1000 + b)
+    lengths = rng.integers(1, 9, size=b) * 32
+    cu = _cu(lengths)
+    cap = vlp.grid_capacity(int(cu[-1]), b, 64)
+    g = vlp.build_ragged_grid(cu.to(DEV), 64, grid_cap=cap)
+    bo, gm, to = oracle.build_ragged_grid(cu.numpy(), 64)
+    assert np.array_equal(g.block_offsets.cpu().numpy(), bo)
+    assert np.array_equal(g.grid_mapping.cpu().numpy()[:len(gm)], gm)
+    assert np.array_equal(g.tile_order.cpu().numpy()[:len(to)], to)
+
+
 def test_device_grid_natural_order_beyond_sort_limit():
     rng = np.random.default_rng(9)
     b = vlp.VLP_DEVICE_SORT_MAX_SEQS + 5
