@@ -250,6 +250,37 @@ def padded_comparator(wl, q, k, v, reps: int, first_token: bool = False):
     return total_ms, backend_used
 
 
+def torch_varlen_comparator(wl, q, k, v, cu, ours, reps: int):
+    """PyTorch's own variable-length flash-attention forward
+    (torch.ops.aten._flash_attention_forward with cumulative sequence
+    lengths; this build's ROCm backend) on the same packed q/k/v: the best
+    per-kernel time of `reps` rounds of 5 launches (HIP events) and the
+    largest absolute difference from this library's output.  Self-attention
+    in 16-bit types only (the op takes one cu_seqlens per side and no fp32)."""
+    import torch
+
+    lmax = int(wl.max_len)
+
+    def run():
+        return torch.ops.aten._flash_attention_forward(q, k, v, cu, cu, lmax, lmax, 0.0, wl.causal, False,
+                                                       scale=wl.scale)[0]
+
+    out = run()
+    torch.cuda.synchronize()
+    diff = float((out.float() - ours.float()).abs().max().item())
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 5
+        best = t if best is None else min(best, t)
+    return best, diff
+
+
 def envelope_own_comparator(wl, dev, reps: int, first_token: bool = False):
     """This library's own forward over the padded envelope: every sequence
     padded to L_max (queries to the longest query length), cu_seqlens =
@@ -801,6 +832,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="zipf", help="tiny | graph | encoder | zipf | skewed | cross")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded SDPA comparator")
+    ap.add_argument("--torch-varlen", action="store_true",
+                    help="also time PyTorch's own varlen flash-attention forward on the same packed batch "
+                         "(16-bit self-attention workloads; off by default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
@@ -1031,6 +1065,13 @@ def main() -> int:
         log("[bench] own kernel over the padded envelope")
         envelope_ms = envelope_own_comparator(wl, dev, reps=3, first_token=ft)
     torch.cuda.synchronize()
+    varlen_ms = varlen_diff = None
+    if args.torch_varlen:
+        if ft or wl.lengths_q is not None or wl.dtype not in ("bf16", "fp16"):
+            log("[bench] --torch-varlen applies to 16-bit self-attention without first-token mode; skipped")
+        else:
+            log("[bench] torch varlen flash-attention comparator")
+            varlen_ms, varlen_diff = torch_varlen_comparator(wl, q, k, v, cu_dev, out, reps=3)
 
     cpu = None
     if not args.no_cpu:
@@ -1081,6 +1122,9 @@ def main() -> int:
         "padded_backend": padded_backend,
         "envelope_own_ms": None if envelope_ms is None else round(envelope_ms, 3),
         "speedup_vs_envelope_own": None if envelope_ms is None else round(envelope_ms / kernel_ms, 3),
+        **({} if varlen_ms is None else {"torch_varlen_flash_ms": round(varlen_ms, 4),
+                                         "speedup_vs_torch_varlen": round(varlen_ms / kernel_ms, 3),
+                                         "torch_varlen_max_abs_diff": varlen_diff}),
         "kernel_ms": round(kernel_ms, 4),
         "kernel_timing": ("device-grid calls minus grid builds timed alone (grid build "
                           f"{grid_build_ms:.4f} ms)" if grid_build_ms is not None else "cached-grid launches"),
