@@ -819,6 +819,7 @@ def bench_matmul(args, wl, dev) -> int:
         "vs_library_gemm": round(lib_ms / ms, 3),
         "algorithmic_gflop": round(flops / 1e9, 3),
         "compulsory_gb": round(nbytes / 1e9, 4),
+        "library_build": vlp.build_info(),
         "note": "each timed call includes the device grid build (~10 us)",
     }
     print(json.dumps(rec), flush=True)
