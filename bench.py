@@ -21,6 +21,12 @@ Also measured in the same run:
     ("DanLing NestedTensor", Appendix C.8: padded attention is masked SDPA over
     the padded envelope), inputs scattered before timing;
   * the CPU oracle on a bounded sample of the same workload (cpu_baseline).
+  * the ceilings as this GPU reaches them (measured_peak): the matrix-core
+    rate of the element type's MFMA instruction from the library's
+    calibration launch, and a plain device copy's streaming rate; the
+    attainable rate min(MFMA peak, arithmetic intensity x HBM rate) from the
+    datasheet figures and from the measured ones (attainable), with the
+    kernel's fraction of each.
 
 Prints ONE JSON line.  Default workload: the Zipf decoder batch (64 sequences,
 Zipf s = 1 over 65,536 tokens, 16 heads x 128, causal, bf16).
@@ -104,6 +110,59 @@ def workload_flops(wl, heads: int, first_token: bool = False) -> float:
 def compulsory_bytes(rows_q: int, total_k: int, heads: int, head_dim: int, elt: int) -> float:
     """q, k, v read once, out written once, lse written once."""
     return (2.0 * rows_q + 2.0 * total_k) * heads * head_dim * elt + 4.0 * rows_q * heads
+
+
+def measured_peaks(dev, dtype: str):
+    """The two ceilings as this GPU reaches them now, each timed with HIP
+    events on the stream the work runs on: the matrix-core rate of the
+    element type's MFMA instruction (vlp_mfma_rate: one workgroup of eight
+    waves per CU, four independent products per wave, no memory traffic) and
+    the streaming rate of a plain 1 GiB device copy (bytes read + written)."""
+    import torch
+    import variable_length_packed_pack_amd as vlp
+
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    iters = 8192 if dtype == "fp32" else 16384
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    flops = vlp.mfma_rate(tdt, cus, iters, sink)
+    mfma_s = timed(lambda: vlp.mfma_rate(tdt, cus, iters, sink), 2, 5)
+    del sink
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    copy_s = timed(lambda: dst.copy_(src), 2, 5)
+    del src, dst
+    return {"mfma_tflops": round(flops / mfma_s / 1e12, 1), "copy_gbs": round(2 * nbytes / copy_s / 1e9, 1),
+            "method": f"vlp_mfma_rate ({dtype} MFMA, {cus} workgroups x 8 waves x {iters} rounds of 4 independent "
+                      "products) and a 1 GiB device copy, HIP events, 5 launches each after 2 warm-ups"}
+
+
+def attainable(flops: float, nbytes: float, achieved_tflops: float, peak_tflops: float, peaks):
+    """Attainable rate = min(MFMA peak, arithmetic intensity x HBM rate), from
+    the datasheet figures and, beside them, from the measured ones; and the
+    kernel's fraction of each."""
+    ai = flops / nbytes
+    bound = min(peak_tflops, ai * HBM_PEAK_GBS / 1e3)
+    out = {"ai_flop_per_byte": round(ai, 2), "datasheet_tflops": round(bound, 2),
+           "frac": round(achieved_tflops / bound, 4)}
+    if peaks is not None:
+        mb = min(peaks["mfma_tflops"], ai * peaks["copy_gbs"] / 1e3)
+        out.update({"measured_tflops": round(mb, 2), "frac_measured": round(achieved_tflops / mb, 4)})
+    return out
 
 
 def traffic_from_profile(workload: str, src_hash: str, kernel: str = "attn_fwd"):
@@ -513,6 +572,9 @@ def bench_backward(args, wl, dev) -> int:
     src_hash = kernel_source_hash(KERNEL_SOURCES_BWD)
     traffic = traffic_from_profile(args.workload, src_hash, kernel="attn_bwd_dkdv")
     log(f"[bench] backward step {ms_per_step:.3f} ms  dkdv {kernel_ms['dkdv']:.3f} ms  dq {kernel_ms['dq']:.3f} ms")
+    peaks = None if args.no_peaks else measured_peaks(dev, wl.dtype)
+    if peaks is not None:
+        peaks["frac_mfma"] = round(roof["achieved"] / peaks["mfma_tflops"], 4)
 
     padded_ms, padded_backend = (None, "skipped")
     if not args.no_padded:
@@ -540,6 +602,7 @@ def bench_backward(args, wl, dev) -> int:
         "config": {"workload": wl.name, "pass": "backward", "num_seqs": b, "total_tokens": t,
                    "max_seqlen": wl.max_len, "heads": h, "head_dim": d, "causal": wl.causal, "block_m": bm},
         "roofline": {**roof, "traffic": traffic},
+        "measured_peak": peaks,
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
         "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
         "padded_ms": None if padded_ms is None else round(padded_ms, 3),
@@ -837,6 +900,8 @@ def main() -> int:
                     help="also time PyTorch's own varlen flash-attention forward on the same packed batch "
                          "(16-bit self-attention workloads; off by default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA and device-copy ceilings (measured_peak, attainable.*measured)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (approx.)")
     ap.add_argument("--kernel-only-reps", type=int, default=0, help="attention-kernel launches (0 = steps)")
     ap.add_argument("--first-token", action="store_true",
@@ -1046,6 +1111,12 @@ def main() -> int:
         src_hash = kernel_source_hash(KERNEL_SOURCES_F32 if wl.dtype == "fp32" else KERNEL_SOURCES)
         traffic = traffic_from_profile(args.workload, src_hash)
     log(f"[bench] step {ms_per_step:.3f} ms  kernel {kernel_ms:.3f} ms  {achieved:.1f} TFLOP/s kernel-only")
+    peaks = None if args.no_peaks else measured_peaks(dev, wl.dtype)
+    if peaks is not None:
+        if ft:
+            peaks["frac_copy"] = round(roof["achieved"] / peaks["copy_gbs"], 4)
+        else:
+            peaks["frac_mfma"] = round(achieved / peaks["mfma_tflops"], 4)
     trace = trace_of_bench(args.workload + ("_first_token" if ft else ""), vlp.build_info(),
                            kernel="attn_first_token" if ft else "attn_fwd")
     if trace is not None and not ft:
@@ -1117,6 +1188,8 @@ def main() -> int:
             "schedule": schedule,
         },
         "roofline": {**roof, "traffic": traffic},
+        "measured_peak": peaks,
+        "attainable": attainable(flops, nbytes, achieved, PEAK_TFLOPS[wl.dtype], peaks),
         "cpu_baseline": None if cpu is None else {k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
         "speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms_per_step, 3),
         "padded_ms": None if padded_ms is None else round(padded_ms, 3),

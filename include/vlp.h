@@ -614,6 +614,29 @@ vlp_status vlp_ragged_matmul_persistent(int32_t dtype, const void* x, const void
 vlp_status vlp_cu_seqlens_from_ids(const int32_t* ids, int64_t num_tokens, int32_t max_seqs, int32_t* cu_seqlens,
                                    int32_t* num_seqs, void* stream);
 
+/*
+ * vlp_mfma_rate -- the matrix-core rate at the running clock, the measured
+ * ceiling beside the datasheet peak for roofline reporting (not an operation
+ * of the pages: a calibration launch for measurement tools).  One launch of
+ * `blocks` workgroups of eight waves (two per SIMD; one workgroup per CU at
+ * a time); every wave runs `iters` rounds of four
+ * independent products with the instruction the attention kernels use for
+ * `dtype` (32x32x16 bf16 / fp16, 32x32x2 fp32) on register operands, with no
+ * memory traffic until each thread writes one float of its sums to `sink`.
+ * The caller times it on `stream` and divides *flops by the time.
+ *
+ *   dtype   VLP_FP32, VLP_FP16 or VLP_BF16.
+ *   blocks  1 .. 65536 (the CU count keeps every SIMD busy).
+ *   iters   1 .. 1,048,576.
+ *   sink    device float [blocks * 512], overwritten (values meaningless).
+ *   flops   host double: receives the flop count of the launch
+ *           (2 * 32 * 32 * K per product, K = 16 for 16-bit and 2 for fp32).
+ * Errors: other dtype -> VLP_ERR_UNSUPPORTED; NULL sink or flops ->
+ * VLP_ERR_NULL; blocks or iters out of range -> VLP_ERR_INVALID; launch
+ * failure -> VLP_ERR_HIP.
+ */
+vlp_status vlp_mfma_rate(int32_t dtype, int32_t blocks, int32_t iters, float* sink, double* flops, void* stream);
+
 /* vlp_build_info -- a static string "csrc=<hash> arch=gfx950" naming the
  * sources this library was built from: <hash> is the first 16 hex digits of
  * a SHA-256 over the library's source files and this header (the build

@@ -579,3 +579,21 @@ def test_loaded_library_matches_sources():
     info = vlp.build_info()
     assert info == f"csrc={source_hash()} arch=gfx950", info
     assert vlp.check_library_current() == source_hash()
+
+
+def test_mfma_rate_validates_before_any_launch():
+    """The calibration entry point checks every argument on the host: bad
+    values return their status without a HIP call (safe without a GPU)."""
+    lib = _lib.load()
+    flops = ctypes.c_double(-1.0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    fp = ctypes.addressof(flops)
+    assert lib.vlp_mfma_rate(7, 256, 10, fake, fp, None) == _lib.VLP_ERR_UNSUPPORTED
+    assert lib.vlp_mfma_rate(-1, 256, 10, fake, fp, None) == _lib.VLP_ERR_UNSUPPORTED
+    assert lib.vlp_mfma_rate(_lib.VLP_BF16, 256, 10, None, fp, None) == _lib.VLP_ERR_NULL
+    assert lib.vlp_mfma_rate(_lib.VLP_BF16, 256, 10, fake, None, None) == _lib.VLP_ERR_NULL
+    assert lib.vlp_mfma_rate(_lib.VLP_BF16, 0, 10, fake, fp, None) == _lib.VLP_ERR_INVALID
+    assert lib.vlp_mfma_rate(_lib.VLP_FP16, (1 << 16) + 1, 10, fake, fp, None) == _lib.VLP_ERR_INVALID
+    assert lib.vlp_mfma_rate(_lib.VLP_FP32, 256, 0, fake, fp, None) == _lib.VLP_ERR_INVALID
+    assert lib.vlp_mfma_rate(_lib.VLP_FP32, 256, (1 << 20) + 1, fake, fp, None) == _lib.VLP_ERR_INVALID
+    assert flops.value == -1.0  # nothing written on a failed check

@@ -84,6 +84,22 @@ def build_info() -> str:
     return _lib.load().vlp_build_info().decode()
 
 
+def mfma_rate(dtype: torch.dtype, blocks: int, iters: int, sink: torch.Tensor) -> float:
+    """One calibration launch on the current stream: ``blocks`` workgroups
+    each running ``iters`` rounds of independent MFMA products of ``dtype``'s
+    instruction.  ``sink``: float32 device tensor of at least blocks * 512
+    elements (overwritten).  Returns the launch's flop count; the caller
+    times the launch."""
+    if sink.dtype != torch.float32 or not sink.is_cuda or not sink.is_contiguous():
+        raise TypeError("sink must be a contiguous float32 device tensor")
+    if sink.numel() < int(blocks) * 512:
+        raise ValueError("sink needs blocks * 512 elements")
+    flops = ctypes.c_double(0.0)
+    _lib.check(_lib.load().vlp_mfma_rate(_DTYPE_CODES.get(dtype, -1), int(blocks), int(iters), _ptr(sink),
+                                         ctypes.addressof(flops), _stream_handle(sink.device)), "mfma_rate")
+    return float(flops.value)
+
+
 def check_library_current() -> str:
     """Raise unless the loaded libvlp.so was built from the sources in this
     tree (its compiled-in hash equals build.source_hash()); returns the hash."""

@@ -101,6 +101,7 @@ SIGNATURES = {
                                                       ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_size_t,
                                                       ctypes.c_int32, _vp]),
     "vlp_cu_seqlens_from_ids": (ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+    "vlp_mfma_rate": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
     "vlp_build_info": (ctypes.c_char_p, []),
     "vlp_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }

@@ -47,6 +47,7 @@ SOURCES = [
     "seq_ids.hip",
     "cu_check.hip",
     "noalloc.hip",
+    "calibrate.hip",
 ]
 
 

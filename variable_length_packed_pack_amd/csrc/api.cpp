@@ -27,6 +27,9 @@ vlp_status hip_status(hipError_t e) {
   return VLP_ERR_HIP;
 }
 
+constexpr int32_t kMfmaRateMaxBlocks = 1 << 16;
+constexpr int32_t kMfmaRateMaxIters = 1 << 20;
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // VLP_CHECK=1 (any value but "0"): check device cu_seqlens contents before
@@ -464,6 +467,20 @@ extern "C" vlp_status vlp_varlen_attn_fwd_grid(int32_t dtype, const void* q, con
 #ifndef VLP_SOURCE_HASH
 #define VLP_SOURCE_HASH "unknown"
 #endif
+
+namespace vlp {
+hipError_t launch_mfma_rate(int dtype, int blocks, int iters, float* sink, hipStream_t s);
+double mfma_rate_flops(int dtype, int blocks, int iters);
+}  // namespace vlp
+
+extern "C" vlp_status vlp_mfma_rate(int32_t dtype, int32_t blocks, int32_t iters, float* sink, double* flops,
+                                    void* stream) {
+  if (dtype != VLP_FP32 && dtype != VLP_FP16 && dtype != VLP_BF16) return VLP_ERR_UNSUPPORTED;
+  if (!sink || !flops) return VLP_ERR_NULL;
+  if (blocks < 1 || blocks > kMfmaRateMaxBlocks || iters < 1 || iters > kMfmaRateMaxIters) return VLP_ERR_INVALID;
+  *flops = vlp::mfma_rate_flops(dtype, blocks, iters);
+  return hip_status(vlp::launch_mfma_rate(dtype, blocks, iters, sink, static_cast<hipStream_t>(stream)));
+}
 
 extern "C" const char* vlp_build_info(void) { return "csrc=" VLP_SOURCE_HASH " arch=gfx950"; }
 
