@@ -49,3 +49,15 @@ def test_attainable_on_both_sides_of_the_ridge():
     assert b["datasheet_tflops"] == 800.0 and b["frac"] == 0.5
     assert b["measured_tflops"] == 500.0 and b["frac_measured"] == 0.8
     assert "measured_tflops" not in bench.attainable(1e11, 1e9, 400.0, 2500.0, None)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
