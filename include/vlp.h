@@ -27,9 +27,12 @@
  *   - Device entry points only enqueue work on `stream` (a hipStream_t passed
  *     as void*, NULL = the null stream); they never synchronise and never read
  *     device memory on the host, so the values in device buffers (cu_seqlens
- *     in particular) are NOT validated: out-of-contract values give undefined
- *     output.  Every argument the host can see is validated before any HIP
- *     call, and a failed check returns a status without touching the GPU.
+ *     in particular) are NOT validated.  Out-of-contract values are undefined
+ *     behaviour: boundaries beyond the rows of q, k or v (say, a
+ *     cross-attention batch's key boundaries passed as its query boundaries)
+ *     make the kernels read and write outside those buffers, which faults the
+ *     GPU.  Every argument the host can see is validated before any HIP call,
+ *     and a failed check returns a status without touching the GPU.
  *   - Debugging aid: with VLP_CHECK=1 in the environment, the attention,
  *     gradient and ragged-matmul entry points first check the cu_seqlens
  *     contents on the device (cu[0] == 0, non-decreasing, cu[num_seqs] no
